@@ -1,0 +1,313 @@
+/*
+ * nvfp4_oracle.c -- CPU oracle for the grouped, row-scaled (per-token) NVFP4
+ * amax + cast of packed MoE activations.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * statement of what the GPU path must compute, used by the tests, by the
+ * smoke check and by the benchmark's CPU-baseline leg.  Nothing on the
+ * product path may link, load or call it, and it shares no code, header,
+ * table or helper with the HIP library.  It is compiled with
+ * `gcc -O2 -ffp-contract=off` (no -ffast-math, no FMA contraction), so every
+ * float expression below is exactly one IEEE-754 binary32 operation with
+ * round-to-nearest-even, as written.
+ *
+ * Sources (the pages this follows; cited by page title and section):
+ *  - "[Common] Single-launch grouped row-scaled NVFP4 cast" (TransformerEngine
+ *    issue 3649), Description: a grouped amax over the packed (sum_M, K)
+ *    buffer yields a rowwise [sum_M] and a columnwise [num_tensors*K] amax,
+ *    then a grouped cast consumes them; a graph-safe twin reads the routing
+ *    from device offsets and is byte-identical.
+ *  - "Implement per-token NVFP4 fprop recipe" (TransformerEngine PR 2931),
+ *    Description and Important Files Changed: one amax per row replaces the
+ *    per-tensor amax; FP4 data with FP8 (E4M3) block scales; the dequant
+ *    looks the amax up by row index.
+ *  - "[PyTorch] Enable NVFP4 row-scaled (per-token) backward for
+ *    GroupedLinear" (TransformerEngine PR 3324), Greptile Summary: the
+ *    columnwise (transposed) operand carries a per-column amax.
+ *  - "Make CustomRecipe usable for grouped GEMM ..." (TransformerEngine PR
+ *    3824), Changes item 2: a 0-element split must not fail.
+ *
+ * The numerics (the pages print no formula; this is the project's fixed
+ * reading, stated once here and in the design notes):
+ *   line scale        s = A / (6 * 448)            (A = the line's amax)
+ *   block decode      t = (b / 6) / s              (b = the block's amax)
+ *                     S = E4M3FN(t), round to nearest, ties to even,
+ *                         saturating at 448
+ *                     d = value(S) * s
+ *                     m = 1 / d  (0 when d == 0; clamped to FLT_MAX)
+ *   element           v = x * m,  code = sign(v) | E2M1(|v|), nearest with
+ *                         ties to the even code, saturating at 6
+ *   dequant           x^ = (value(code) * value(S)) * (A / (6 * 448))
+ * A "line" is a row of X (rowwise) or one column of one expert's rows
+ * (columnwise); blocks are 16 consecutive elements of a line.
+ *
+ * Parity pins: every function here is pinned by the CPU tests (exhaustive
+ * and special-case checks of the two conversions against their definitions
+ * and against torch's float8_e4m3fn cast, closed-form round trips, an
+ * independent numpy brute force, grouped == per-expert loop, the half-gap
+ * error bound and hand-worked golden rows).  No function is left unpinned.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+
+/* FP4 (E2M1) and FP8 (E4M3) maxima; their product is the line-scale divisor. */
+static const float kFp4Max = 6.0f;
+static const float kE4m3Max = 448.0f;
+
+/* ---------------------------------------------------------------- widening */
+
+/* bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 one. */
+static float bf16_value(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* ------------------------------------------------------------- E4M3FN code */
+
+/* Value of an E4M3FN code (sign 0): 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals when the exponent field is 0; code 0x7F is NaN and is
+ * never produced here. */
+double oracle_e4m3_value(int code) {
+  int e = (code >> 3) & 15;
+  int f = code & 7;
+  if (e == 0) return ldexp((double)f, -9);          /* f/8 * 2^(1-7) */
+  return ldexp(1.0 + f / 8.0, e - 7);
+}
+
+/* Nearest E4M3FN code to t >= 0, ties to the even code, saturating: any t at
+ * or above the largest finite value 448 gives 0x7E.  Written as a scan over
+ * the 127 non-negative finite codes so that it can be checked by eye. */
+int oracle_e4m3_encode(float t) {
+  if (!(t >= 0.0f)) return -1; /* negative or NaN: outside the contract */
+  if (t >= kE4m3Max) return 0x7E;
+  double td = (double)t;
+  for (int c = 0; c < 0x7E; ++c) {
+    double lo = oracle_e4m3_value(c), hi = oracle_e4m3_value(c + 1);
+    if (td > hi) continue;
+    double mid = 0.5 * (lo + hi); /* exact in double */
+    if (td < mid) return c;
+    if (td > mid) return c + 1;
+    return (c % 2 == 0) ? c : c + 1; /* tie: even code */
+  }
+  return 0x7E;
+}
+
+/* ------------------------------------------------------------- E2M1 code */
+
+/* The eight non-negative E2M1 values, indexed by the 3-bit magnitude code. */
+static const double kE2m1Grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double oracle_e2m1_value(int code) {
+  double v = kE2m1Grid[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* Magnitude code of the nearest E2M1 value to a >= 0, ties to the even code,
+ * saturating: a >= 6 (including +inf) gives 7. */
+int oracle_e2m1_encode_mag(float a) {
+  if (!(a >= 0.0f)) return -1;
+  if (a >= 6.0f) return 7;
+  double ad = (double)a;
+  for (int c = 0; c < 7; ++c) {
+    double lo = kE2m1Grid[c], hi = kE2m1Grid[c + 1];
+    if (ad > hi) continue;
+    double mid = 0.5 * (lo + hi);
+    if (ad < mid) return c;
+    if (ad > mid) return c + 1;
+    return (c % 2 == 0) ? c : c + 1;
+  }
+  return 7;
+}
+
+/* 4-bit code of v: sign bit of v in bit 3, magnitude code in bits 0..2. */
+int oracle_e2m1_encode(float v) {
+  int sign = signbit(v) ? 8 : 0;
+  return sign | oracle_e2m1_encode_mag(fabsf(v));
+}
+
+/* ------------------------------------------------------------ line encode */
+
+/* Line scale s = A / (6*448): the per-row (or per-column) scale that replaces
+ * the per-tensor one. */
+float oracle_line_scale(float amax) { return amax / (kFp4Max * kE4m3Max); }
+
+/* Block step for block amax b on a line with scale s: returns the E4M3 code
+ * and writes the element multiplier m = 1/d. */
+int oracle_block_scale(float b, float s, float* m_out) {
+  float t = (s == 0.0f) ? 0.0f : (b / kFp4Max) / s;
+  int S = oracle_e4m3_encode(t);
+  float d = (float)oracle_e4m3_value(S) * s;
+  float m = 0.0f;
+  if (d != 0.0f) m = fminf(1.0f / d, FLT_MAX);
+  *m_out = m;
+  return S;
+}
+
+/* Encode one line of n values (n a multiple of 16) with line amax A.
+ * codes: n/2 bytes, element 2j in the low nibble of byte j, element 2j+1 in
+ * the high nibble.  scales: n/16 E4M3 codes. */
+int oracle_encode_line(const float* L, int64_t n, float A, uint8_t* codes,
+                       uint8_t* scales) {
+  if (n < 0 || n % 16 != 0) return ORACLE_EINVAL;
+  float s = oracle_line_scale(A);
+  for (int64_t j = 0; j < n / 16; ++j) {
+    const float* blk = L + 16 * j;
+    float b = 0.0f;
+    for (int i = 0; i < 16; ++i) b = fmaxf(b, fabsf(blk[i]));
+    float m;
+    int S = oracle_block_scale(b, s, &m);
+    scales[j] = (uint8_t)S;
+    for (int i = 0; i < 16; i += 2) {
+      int c0 = oracle_e2m1_encode(blk[i] * m);
+      int c1 = oracle_e2m1_encode(blk[i + 1] * m);
+      codes[8 * j + i / 2] = (uint8_t)(c0 | (c1 << 4));
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Dequantize one encoded line back to fp32 with the same A. */
+int oracle_decode_line(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                       float A, float* out) {
+  if (n < 0 || n % 16 != 0) return ORACLE_EINVAL;
+  float s = oracle_line_scale(A);
+  for (int64_t i = 0; i < n; ++i) {
+    int byte = codes[i / 2];
+    int code = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+    float q = (float)oracle_e2m1_value(code);
+    float S = (float)oracle_e4m3_value(scales[i / 16]);
+    out[i] = (q * S) * s;
+  }
+  return ORACLE_OK;
+}
+
+/* --------------------------------------------------------------- grouping */
+
+/* Validate the host split list: E >= 1, splits >= 0, multiples of 128,
+ * summing to sum_m; K a positive multiple of 16. */
+static int check_args(int64_t sum_m, int64_t k, int32_t E,
+                      const int64_t* splits) {
+  if (E < 1 || k <= 0 || k % 16 != 0 || sum_m < 0 || splits == NULL)
+    return ORACLE_EINVAL;
+  int64_t tot = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    if (splits[e] < 0 || splits[e] % 128 != 0) return ORACLE_EINVAL;
+    tot += splits[e];
+  }
+  return tot == sum_m ? ORACLE_OK : ORACLE_EINVAL;
+}
+
+/* Amax of one row of X (bf16, row-major with row length k). */
+float oracle_row_amax(const uint16_t* x, int64_t k, int64_t r) {
+  float a = 0.0f;
+  for (int64_t c = 0; c < k; ++c) a = fmaxf(a, fabsf(bf16_value(x[r * k + c])));
+  return a;
+}
+
+/* Amax of column c over rows [r0, r0 + m). */
+float oracle_col_amax(const uint16_t* x, int64_t k, int64_t c, int64_t r0,
+                      int64_t m) {
+  float a = 0.0f;
+  for (int64_t r = r0; r < r0 + m; ++r) a = fmaxf(a, fabsf(bf16_value(x[r * k + c])));
+  return a;
+}
+
+/* Grouped amax: row_amax[r] over each row; col_amax[e*k + c] over the rows of
+ * expert e (0 for an expert with no rows).  Either output may be NULL. */
+int oracle_group_amax(const uint16_t* x, int64_t sum_m, int64_t k, int32_t E,
+                      const int64_t* splits, float* row_amax, float* col_amax) {
+  int rc = check_args(sum_m, k, E, splits);
+  if (rc != ORACLE_OK) return rc;
+  if (row_amax)
+    for (int64_t r = 0; r < sum_m; ++r) row_amax[r] = oracle_row_amax(x, k, r);
+  if (col_amax) {
+    int64_t r0 = 0;
+    for (int32_t e = 0; e < E; ++e) {
+      for (int64_t c = 0; c < k; ++c)
+        col_amax[(int64_t)e * k + c] = oracle_col_amax(x, k, c, r0, splits[e]);
+      r0 += splits[e];
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Rowwise cast of row r: k/2 data bytes and k/16 scales. */
+int oracle_cast_row(const uint16_t* x, int64_t k, int64_t r, float A,
+                    uint8_t* data, uint8_t* scales) {
+  float* L = (float*)malloc(sizeof(float) * (size_t)(k > 0 ? k : 1));
+  if (!L) return ORACLE_EINVAL;
+  for (int64_t c = 0; c < k; ++c) L[c] = bf16_value(x[r * k + c]);
+  int rc = oracle_encode_line(L, k, A, data, scales);
+  free(L);
+  return rc;
+}
+
+/* Columnwise cast of column c of the expert owning rows [r0, r0 + m):
+ * m/2 data bytes and m/16 scales (one line of the transposed expert). */
+int oracle_cast_col(const uint16_t* x, int64_t k, int64_t c, int64_t r0,
+                    int64_t m, float A, uint8_t* data, uint8_t* scales) {
+  float* L = (float*)malloc(sizeof(float) * (size_t)(m > 0 ? m : 1));
+  if (!L) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < m; ++r) L[r] = bf16_value(x[(r0 + r) * k + c]);
+  int rc = oracle_encode_line(L, m, A, data, scales);
+  free(L);
+  return rc;
+}
+
+/* Grouped cast.  Rowwise outputs: data [sum_m, k/2], scales [sum_m, k/16].
+ * Columnwise outputs, expert e owning rows [r_e, r_e + M_e): data [k, M_e/2]
+ * at byte k*r_e/2, scales [k, M_e/16] at byte k*r_e/16.  A direction is
+ * produced when its data pointer is non-NULL (its scale pointer and amax must
+ * then be non-NULL too). */
+int oracle_group_cast(const uint16_t* x, int64_t sum_m, int64_t k, int32_t E,
+                      const int64_t* splits, const float* row_amax,
+                      const float* col_amax, uint8_t* row_data,
+                      uint8_t* row_scale, uint8_t* col_data,
+                      uint8_t* col_scale) {
+  int rc = check_args(sum_m, k, E, splits);
+  if (rc != ORACLE_OK) return rc;
+  if (row_data) {
+    if (!row_scale || !row_amax) return ORACLE_EINVAL;
+    for (int64_t r = 0; r < sum_m; ++r) {
+      rc = oracle_cast_row(x, k, r, row_amax[r], row_data + r * (k / 2),
+                           row_scale + r * (k / 16));
+      if (rc != ORACLE_OK) return rc;
+    }
+  }
+  if (col_data) {
+    if (!col_scale || !col_amax) return ORACLE_EINVAL;
+    int64_t r0 = 0;
+    for (int32_t e = 0; e < E; ++e) {
+      int64_t m = splits[e];
+      uint8_t* d = col_data + k * r0 / 2;
+      uint8_t* sc = col_scale + k * r0 / 16;
+      for (int64_t c = 0; c < k; ++c) {
+        rc = oracle_cast_col(x, k, c, r0, m, col_amax[(int64_t)e * k + c],
+                             d + c * (m / 2), sc + c * (m / 16));
+        if (rc != ORACLE_OK) return rc;
+      }
+      r0 += m;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Batch helpers for the tests (plain loops over the scalar functions). */
+void oracle_e4m3_encode_array(const float* t, int64_t n, int32_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(t[i]);
+}
+void oracle_e2m1_encode_array(const float* v, int64_t n, int32_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_encode(v[i]);
+}
+void oracle_block_scale_array(const float* b, const float* s, int64_t n,
+                              int32_t* S_out, float* m_out) {
+  for (int64_t i = 0; i < n; ++i) S_out[i] = oracle_block_scale(b[i], s[i], &m_out[i]);
+}

@@ -1,0 +1,235 @@
+"""Python access to the C oracle (``nvfp4_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``, never by the product package.  The
+oracle shares no code with the HIP library; see the header of
+``nvfp4_oracle.c`` for what it computes and which page passages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "nvfp4_oracle.c")
+LIB = os.path.join(HERE, "libnvfp4_oracle.so")
+
+# -ffp-contract=off: no FMA contraction, so each float expression in the C
+# source is one IEEE binary32 operation; no -ffast-math, no -march=native.
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11"]
+
+
+def build() -> str:
+    """Compile the oracle with gcc into ``oracle/libnvfp4_oracle.so``."""
+    tmp = LIB + ".tmp"
+    subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_F = ctypes.c_float
+
+
+def lib() -> ctypes.CDLL:
+    """Load the oracle library, building it only if it is not built yet."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        L.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e2m1_value.argtypes = [ctypes.c_int]
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e4m3_encode.argtypes = [_F]
+        L.oracle_e4m3_encode.restype = ctypes.c_int
+        L.oracle_e2m1_encode.argtypes = [_F]
+        L.oracle_e2m1_encode.restype = ctypes.c_int
+        L.oracle_line_scale.argtypes = [_F]
+        L.oracle_line_scale.restype = _F
+        L.oracle_block_scale.argtypes = [_F, _F, ctypes.POINTER(_F)]
+        L.oracle_block_scale.restype = ctypes.c_int
+        L.oracle_encode_line.argtypes = [_P, _I64, _F, _P, _P]
+        L.oracle_decode_line.argtypes = [_P, _P, _I64, _F, _P]
+        L.oracle_row_amax.argtypes = [_P, _I64, _I64]
+        L.oracle_row_amax.restype = _F
+        L.oracle_col_amax.argtypes = [_P, _I64, _I64, _I64, _I64]
+        L.oracle_col_amax.restype = _F
+        L.oracle_group_amax.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P]
+        L.oracle_cast_row.argtypes = [_P, _I64, _I64, _F, _P, _P]
+        L.oracle_cast_col.argtypes = [_P, _I64, _I64, _I64, _I64, _F, _P, _P]
+        L.oracle_group_cast.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
+        L.oracle_e4m3_encode_array.argtypes = [_P, _I64, _P]
+        L.oracle_e2m1_encode_array.argtypes = [_P, _I64, _P]
+        L.oracle_block_scale_array.argtypes = [_P, _P, _I64, _P, _P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (status {rc})")
+
+
+# --------------------------------------------------------------- conversions
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(int(code))
+
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(int(code))
+
+
+def e4m3_encode(t: np.ndarray) -> np.ndarray:
+    t = np.ascontiguousarray(t, dtype=np.float32)
+    out = np.empty(t.shape, dtype=np.int32)
+    lib().oracle_e4m3_encode_array(_ptr(t), t.size, _ptr(out))
+    return out
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.int32)
+    lib().oracle_e2m1_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def line_scale(amax: float) -> np.float32:
+    return np.float32(lib().oracle_line_scale(float(amax)))
+
+
+def block_scale(b: np.ndarray, s: np.ndarray):
+    """Vector form of the block step: returns (E4M3 codes, multipliers m)."""
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    s = np.ascontiguousarray(np.broadcast_to(s, b.shape), dtype=np.float32)
+    S = np.empty(b.shape, dtype=np.int32)
+    m = np.empty(b.shape, dtype=np.float32)
+    lib().oracle_block_scale_array(_ptr(b), _ptr(s), b.size, _ptr(S), _ptr(m))
+    return S, m
+
+
+# ------------------------------------------------------------------- lines
+
+def encode_line(L: np.ndarray, amax: float):
+    L = np.ascontiguousarray(L, dtype=np.float32)
+    n = L.size
+    codes = np.empty(n // 2, dtype=np.uint8)
+    scales = np.empty(n // 16, dtype=np.uint8)
+    _check(lib().oracle_encode_line(_ptr(L), n, float(amax), _ptr(codes), _ptr(scales)), "encode_line")
+    return codes, scales
+
+
+def decode_line(codes: np.ndarray, scales: np.ndarray, n: int, amax: float) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty(n, dtype=np.float32)
+    _check(lib().oracle_decode_line(_ptr(codes), _ptr(scales), n, float(amax), _ptr(out)), "decode_line")
+    return out
+
+
+def row_amax(x: np.ndarray, r: int) -> np.float32:
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    return np.float32(lib().oracle_row_amax(_ptr(x), x.shape[1], int(r)))
+
+
+def col_amax(x: np.ndarray, c: int, r0: int, m: int) -> np.float32:
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    return np.float32(lib().oracle_col_amax(_ptr(x), x.shape[1], int(c), int(r0), int(m)))
+
+
+def cast_row(x: np.ndarray, r: int, amax: float):
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    k = x.shape[1]
+    data = np.empty(k // 2, dtype=np.uint8)
+    sc = np.empty(k // 16, dtype=np.uint8)
+    _check(lib().oracle_cast_row(_ptr(x), k, int(r), float(amax), _ptr(data), _ptr(sc)), "cast_row")
+    return data, sc
+
+
+def cast_col(x: np.ndarray, c: int, r0: int, m: int, amax: float):
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    k = x.shape[1]
+    data = np.empty(m // 2, dtype=np.uint8)
+    sc = np.empty(m // 16, dtype=np.uint8)
+    _check(lib().oracle_cast_col(_ptr(x), k, int(c), int(r0), int(m), float(amax), _ptr(data), _ptr(sc)),
+           "cast_col")
+    return data, sc
+
+
+# ---------------------------------------------------------------- grouped
+
+def group_amax(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool = True):
+    """Grouped amax over packed bf16 bits ``x`` (sum_m, k) with host splits."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    sum_m, k = x.shape
+    sp = np.ascontiguousarray(splits, dtype=np.int64)
+    E = sp.size
+    ra = np.empty(sum_m, dtype=np.float32) if rowwise else None
+    ca = np.empty(E * k, dtype=np.float32) if columnwise else None
+    _check(lib().oracle_group_amax(_ptr(x), sum_m, k, E, _ptr(sp), _ptr(ra), _ptr(ca)), "group_amax")
+    return ra, ca
+
+
+def group_cast(x: np.ndarray, splits, row_amax=None, col_amax=None,
+               rowwise: bool = True, columnwise: bool = True):
+    """Grouped cast.  Returns (row_data, row_scale, col_data, col_scale); the
+    arrays of a direction not requested are None."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    sum_m, k = x.shape
+    sp = np.ascontiguousarray(splits, dtype=np.int64)
+    E = sp.size
+    rd = np.empty((sum_m, k // 2), dtype=np.uint8) if rowwise else None
+    rs = np.empty((sum_m, k // 16), dtype=np.uint8) if rowwise else None
+    cd = np.empty(sum_m * k // 2, dtype=np.uint8) if columnwise else None
+    cs = np.empty(sum_m * k // 16, dtype=np.uint8) if columnwise else None
+    ra = None if row_amax is None else np.ascontiguousarray(row_amax, dtype=np.float32)
+    ca = None if col_amax is None else np.ascontiguousarray(col_amax, dtype=np.float32)
+    _check(lib().oracle_group_cast(_ptr(x), sum_m, k, E, _ptr(sp), _ptr(ra), _ptr(ca),
+                                   _ptr(rd), _ptr(rs), _ptr(cd), _ptr(cs)), "group_cast")
+    return rd, rs, cd, cs
+
+
+def group_quantize(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool = True):
+    """Amax then cast, as one dict of numpy arrays."""
+    ra, ca = group_amax(x, splits, rowwise, columnwise)
+    rd, rs, cd, cs = group_cast(x, splits, ra, ca, rowwise, columnwise)
+    return {"row_amax": ra, "col_amax": ca, "row_data": rd, "row_scale": rs,
+            "col_data": cd, "col_scale": cs}
+
+
+def decode_rowwise(row_data, row_scale, row_amax) -> np.ndarray:
+    """Dequantize the whole rowwise output to fp32 (sum_m, k)."""
+    sum_m = row_data.shape[0]
+    k = row_data.shape[1] * 2
+    out = np.empty((sum_m, k), dtype=np.float32)
+    for r in range(sum_m):
+        out[r] = decode_line(row_data[r], row_scale[r], k, row_amax[r])
+    return out
+
+
+def decode_columnwise(col_data, col_scale, col_amax, splits, k: int):
+    """Dequantize the columnwise output back to the (sum_m, k) layout."""
+    sp = [int(v) for v in splits]
+    sum_m = sum(sp)
+    out = np.empty((sum_m, k), dtype=np.float32)
+    r0 = 0
+    for e, m in enumerate(sp):
+        d = col_data[k * r0 // 2: k * (r0 + m) // 2].reshape(k, m // 2) if m else None
+        s = col_scale[k * r0 // 16: k * (r0 + m) // 16].reshape(k, m // 16) if m else None
+        for c in range(k if m else 0):
+            out[r0:r0 + m, c] = decode_line(d[c], s[c], m, col_amax[e * k + c])
+        r0 += m
+    return out
