@@ -1,0 +1,191 @@
+"""Benchmark of the grouped row-scaled NVFP4 amax + cast on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over the workload: the grouped amax
+(rowwise + per-expert columnwise) then the grouped cast (rowwise +
+transposed), through the C ABI, with the input resident in HBM.  The default
+workload is the DeepSeek-V3-style one-GPU expert share (32 experts, K=7168,
+sum_M=65536, Zipf routing, both directions).  Prints one JSON line.
+
+value = algorithmic bytes per step / time per step, where the algorithmic
+bytes count what the method must move: two reads of x (the column amax needs
+every row of an expert before any of its blocks can be cast), the amax
+vectors written once and read once, and both outputs written once.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "grouped NVFP4 amax+cast HBM GB/s (bytes in+out) and % of MI355X peak BW"
+
+
+def algorithmic_bytes(sum_m: int, k: int, E: int, rowwise: bool, columnwise: bool) -> dict:
+    N = sum_m * k
+    amax_out = (4 * sum_m if rowwise else 0) + (4 * E * k if columnwise else 0)
+    outs = (N // 2 + N // 16) * (int(rowwise) + int(columnwise))
+    amax_k = 2 * N + amax_out                     # read x, write amax
+    cast_k = 2 * N + amax_out + outs              # read x and amax, write data + scales
+    return {"amax_kernel": amax_k, "cast_kernel": cast_k, "step": amax_k + cast_k}
+
+
+def cpu_baseline(w, target_rows: int = 6144) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole experts (in expert order, skipping any that would overshoot) up to
+    ``target_rows`` rows, both directions, one thread."""
+    from oracle import oracle as O
+    offs = np.concatenate([[0], np.cumsum(w.splits)])
+    chosen, rows = [], 0
+    for e, m in enumerate(w.splits):
+        if m and rows + int(m) <= target_rows:
+            chosen.append(e)
+            rows += int(m)
+    xs = np.concatenate([w.x[offs[e]:offs[e + 1]] for e in chosen])
+    sp = [int(w.splits[e]) for e in chosen]
+    t0 = time.perf_counter()
+    O.group_quantize(xs, sp, w.rowwise, w.columnwise)
+    dt = time.perf_counter() - t0
+    b = algorithmic_bytes(rows, w.k, len(sp), w.rowwise, w.columnwise)["step"]
+    return {"value": round(b / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(sp)} whole experts, {rows} of {w.sum_m} rows x K={w.k} "
+                      f"(both directions), single-threaded C oracle, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="deepseek_share",
+                    choices=["deepseek_share", "down_proj", "outliers", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph-replays", type=int, default=100)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from nvfp4_block_scaled_group_amd import binding as B
+    from nvfp4_block_scaled_group_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    w = synth.CONFIGS[args.workload]()
+    splits = [int(v) for v in w.splits]
+    E, k, m = w.num_experts, w.k, w.sum_m
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    out = B.alloc_outputs(m, k, E, w.rowwise, w.columnwise, device=dev)
+    nbytes = algorithmic_bytes(m, k, E, w.rowwise, w.columnwise)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        B.nvfp4_group_amax(x, splits, out["row_amax"], out["col_amax"])
+        if ev is not None:
+            ev[1].record()
+        B.nvfp4_group_cast(x, splits, **out)
+        if ev is not None:
+            ev[2].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    amax_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    cast_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ms_per_step = wall * 1e3 / args.steps
+    value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
+    cast_gbs = nbytes["cast_kernel"] / (cast_ms * 1e-3) / 1e9
+    amax_gbs = nbytes["amax_kernel"] / (amax_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_experts": E, "k": k, "sum_m": m,
+                   "directions": "+".join(d for d, on in (("rowwise", w.rowwise), ("columnwise", w.columnwise))
+                                          if on),
+                   "entry": "nvfp4_group_amax + nvfp4_group_cast (host splits)",
+                   "algorithmic_bytes_per_step": nbytes["step"],
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "kernel": "group_cast_kernel", "achieved": round(cast_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(cast_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_us": round(cast_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": nbytes["cast_kernel"]},
+        "kernels": {"amax (init + group_amax_kernel)": {"avg_us": round(amax_ms * 1e3, 2),
+                                                        "GBps": round(amax_gbs, 2)},
+                    "group_cast_kernel": {"avg_us": round(cast_ms * 1e3, 2), "GBps": round(cast_gbs, 2)}},
+    }
+
+    if args.workload == "deepseek_share" and args.graph_replays > 0:
+        result["graph_replay"] = graph_replay(B, synth, torch, dev, args.graph_replays)
+
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+def graph_replay(B, synth, torch, dev, replays: int) -> dict:
+    """Graph-safe path on the expert-share shapes with gradient-like values:
+    one hipGraph capture of amax + cast, replayed with new routing written to
+    the device offsets before each replay (the offset copy is outside the
+    timed launches)."""
+    print("[bench] graph replay workload", file=sys.stderr, flush=True)
+    w = synth.graph_replay()
+    E, k, m = w.num_experts, w.k, w.sum_m
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    out = B.alloc_outputs(m, k, E, True, True, device=dev)
+    routes = [torch.tensor(B.offsets_from_splits(synth.replay_splits(i)), dtype=torch.int32).pin_memory()
+              for i in range(replays)]
+    d_offs = torch.empty(E, dtype=torch.int32, device=dev)
+    d_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    d_offs.copy_(routes[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.nvfp4_group_quantize_graphsafe(x, E, d_offs, d_status, **out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.nvfp4_group_quantize_graphsafe(x, E, d_offs, d_status, **out)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(replays):
+        d_offs.copy_(routes[i], non_blocking=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in times]))
+    nbytes = algorithmic_bytes(m, k, E, True, True)["step"]
+    return {"workload": w.name, "replays": replays, "ms_per_replay": round(ms, 4),
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 2), "status": int(d_status.item())}
+
+
+if __name__ == "__main__":
+    main()

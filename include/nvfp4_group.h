@@ -1,0 +1,153 @@
+/*
+ * nvfp4_group.h -- C ABI of libnvfp4g.so: grouped, row-scaled (per-token)
+ * NVFP4 amax + cast of packed MoE expert activations/gradients on MI355X.
+ *
+ * What is computed (pages cited by title and section):
+ *  - "[Common] Single-launch grouped row-scaled NVFP4 cast" (TransformerEngine
+ *    issue 3649), Description: one grouped amax launch over the packed
+ *    (sum_M, K) buffer produces a rowwise [sum_M] and a columnwise
+ *    [num_experts * K] amax (both directions in one pass); one grouped cast
+ *    launch consumes them; each has a graph-safe twin that reads the routing
+ *    from device offsets instead of host split metadata, with the same device
+ *    body, so the outputs of the two are byte-identical.
+ *  - "Implement per-token NVFP4 fprop recipe" (TransformerEngine PR 2931),
+ *    Description / Important Files Changed: one fp32 amax per row (token)
+ *    replaces the per-tensor amax; data is FP4 (E2M1) with one FP8 (E4M3)
+ *    scale per 16-element block; dequantisation looks up the amax by row.
+ *  - "[PyTorch] Enable NVFP4 row-scaled (per-token) backward for
+ *    GroupedLinear" (TransformerEngine PR 3324), Greptile Summary: the
+ *    columnwise (transposed) operand is quantised with a per-column amax.
+ *
+ * Numerics, per line (a row of X, or one column of one expert's rows) with
+ * amax A, and per 16-element block of the line with block amax b; every step
+ * is one IEEE binary32 operation, round to nearest even, no FMA contraction,
+ * denormals kept:
+ *     s = A / 2688            (2688 = 6 * 448)
+ *     t = (b / 6) / s         (0 when s == 0)
+ *     S = E4M3FN(t)           nearest, ties to even, saturating at 448 (0x7E)
+ *     d = value(S) * s
+ *     m = 1 / d               (0 when d == 0, at most FLT_MAX)
+ *     code = sign(x*m) << 3 | E2M1(|x*m|)   nearest on {0,.5,1,1.5,2,3,4,6},
+ *                                           ties to the even code, saturating
+ *
+ * Layouts (all row-major, unswizzled; expert e owns rows [r_e, r_e + M_e),
+ * M_e a multiple of 128, experts packed in order):
+ *     x          bf16 bits, [sum_m, k], contiguous, 16-byte aligned
+ *     row_amax   fp32 [sum_m]
+ *     col_amax   fp32 [E * k], expert-major (0 for an expert with no rows)
+ *     row_data   u8 [sum_m, k/2]: element 2j in the low nibble of byte j
+ *     row_scale  u8 [sum_m, k/16]: E4M3FN codes
+ *     col_data   u8, per expert a [k, M_e/2] block (line c = column c of the
+ *                expert, packed along its rows) at byte offset k*r_e/2
+ *     col_scale  u8, per expert a [k, M_e/16] block at byte offset k*r_e/16
+ *
+ * Conventions: every pointer except h_splits is a device pointer owned by
+ * the caller; `stream` is a hipStream_t (NULL = the default stream).  Calls
+ * only enqueue work on `stream` and never synchronise, allocate or read
+ * device memory on the host.  Arguments are checked on the host first and a
+ * call that fails a check enqueues nothing and returns a negative status;
+ * launch failures return NVFP4G_EHIP.  A direction is produced when its data
+ * pointer is non-NULL (its scale pointer and amax must then be non-NULL).
+ */
+#ifndef NVFP4_GROUP_H_
+#define NVFP4_GROUP_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4G_OK 0
+#define NVFP4G_EINVAL (-1)  /* bad size, count, NULL pointer or direction */
+#define NVFP4G_ESPLITS (-2) /* host splits negative, not %128, or sum != sum_m */
+#define NVFP4G_EALIGN (-3)  /* x or an output not suitably aligned */
+#define NVFP4G_EHIP (-4)    /* HIP launch/runtime error */
+
+/* Largest expert count of the host-split calls (the splits travel in the
+ * kernel arguments) and of the graph-safe calls. */
+#define NVFP4G_MAX_EXPERTS_HOST 512
+#define NVFP4G_MAX_EXPERTS_DEVICE 4096
+
+/* Bits ORed into *d_status by the graph-safe calls when the device routing is
+ * invalid; the library never clears them.  With any bit set the call writes
+ * nothing else. */
+#define NVFP4G_DEV_UNALIGNED 1 /* an expert's row count is not a multiple of 128 */
+#define NVFP4G_DEV_NONMONO 2   /* offsets decrease (or the first is negative) */
+#define NVFP4G_DEV_OVERFLOW 4  /* offs[E-1] > m_capacity */
+
+/* Grouped amax ("[Common] Single-launch grouped row-scaled NVFP4 cast",
+ * Description).  x: [sum_m, k] bf16; h_splits: host array of E row counts
+ * (each >= 0, a multiple of 128, summing to sum_m).  Writes
+ * row_amax[r] = max_c |x[r, c]| and col_amax[e*k + c] = max over the rows of
+ * expert e of |x[r, c]| (0 for an expert with no rows).  Either output may
+ * be NULL to skip that direction.  k must be a positive multiple of 16. */
+int nvfp4_group_amax(const uint16_t* x, int64_t sum_m, int64_t k,
+                     int32_t num_experts, const int64_t* h_splits,
+                     float* row_amax, float* col_amax, void* stream);
+
+/* Grouped cast (same page, Description; per-token numerics from "Implement
+ * per-token NVFP4 fprop recipe"; columnwise per-column amax from "Enable
+ * NVFP4 row-scaled (per-token) backward for GroupedLinear").  Consumes the
+ * amax vectors of nvfp4_group_amax and writes the rowwise and/or columnwise
+ * FP4 data and E4M3 scales in the layouts above. */
+int nvfp4_group_cast(const uint16_t* x, int64_t sum_m, int64_t k,
+                     int32_t num_experts, const int64_t* h_splits,
+                     const float* row_amax, const float* col_amax,
+                     uint8_t* row_data, uint8_t* row_scale, uint8_t* col_data,
+                     uint8_t* col_scale, void* stream);
+
+/* Graph-safe grouped amax (same page, Description: routing read from device
+ * offsets so a captured graph replays under changed routing).  d_offs:
+ * device int32[E], inclusive row ends (expert e owns rows
+ * [offs[e-1], offs[e]), offs[-1] = 0).  m_capacity (a multiple of 128) sizes
+ * the buffers: x and row_amax hold m_capacity rows; rows at or beyond
+ * offs[E-1] are neither read nor written.  col_amax is fully written.  The
+ * routing is checked on the device; if it is invalid, bits are ORed into
+ * *d_status (a device int32 the caller zeroes) and nothing else is written.
+ * Output bytes equal those of nvfp4_group_amax for the same routing. */
+int nvfp4_group_amax_graphsafe(const uint16_t* x, int64_t m_capacity, int64_t k,
+                               int32_t num_experts, const int32_t* d_offs,
+                               float* row_amax, float* col_amax,
+                               int32_t* d_status, void* stream);
+
+/* Graph-safe grouped cast: as nvfp4_group_cast with the routing taken from
+ * d_offs (see nvfp4_group_amax_graphsafe).  row_data/row_scale hold
+ * m_capacity rows; col_data/col_scale hold k*m_capacity/2 and
+ * k*m_capacity/16 bytes, of which the first k*offs[E-1]/2 (/16) are written.
+ * Output bytes equal those of nvfp4_group_cast for the same routing. */
+int nvfp4_group_cast_graphsafe(const uint16_t* x, int64_t m_capacity, int64_t k,
+                               int32_t num_experts, const int32_t* d_offs,
+                               const float* row_amax, const float* col_amax,
+                               uint8_t* row_data, uint8_t* row_scale,
+                               uint8_t* col_data, uint8_t* col_scale,
+                               int32_t* d_status, void* stream);
+
+/* Amax + cast in one call (both launches of the grouped cast page's
+ * Description, enqueued back to back).  When no columnwise output is
+ * requested the rowwise amax and cast run as one fused pass over x, the
+ * one-pass-per-row form of "Implement per-token NVFP4 fprop recipe",
+ * Important Files Changed; row_amax is still written. */
+int nvfp4_group_quantize(const uint16_t* x, int64_t sum_m, int64_t k,
+                         int32_t num_experts, const int64_t* h_splits,
+                         float* row_amax, float* col_amax, uint8_t* row_data,
+                         uint8_t* row_scale, uint8_t* col_data,
+                         uint8_t* col_scale, void* stream);
+
+/* Graph-safe form of nvfp4_group_quantize. */
+int nvfp4_group_quantize_graphsafe(const uint16_t* x, int64_t m_capacity,
+                                   int64_t k, int32_t num_experts,
+                                   const int32_t* d_offs, float* row_amax,
+                                   float* col_amax, uint8_t* row_data,
+                                   uint8_t* row_scale, uint8_t* col_data,
+                                   uint8_t* col_scale, int32_t* d_status,
+                                   void* stream);
+
+/* Static description of a status code. */
+const char* nvfp4_group_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_GROUP_H_ */

@@ -1,0 +1,117 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every
+entry point declared in include/*.h, and rejects bad arguments on the host
+before any HIP call is made."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "nvfp4_block_scaled_group_amd", "libnvfp4g.so")
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nvfp4_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from nvfp4_block_scaled_group_amd import build
+        build.build()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == {
+        "nvfp4_group_amax", "nvfp4_group_cast", "nvfp4_group_amax_graphsafe",
+        "nvfp4_group_cast_graphsafe", "nvfp4_group_quantize", "nvfp4_group_quantize_graphsafe",
+        "nvfp4_group_strerror",
+    }
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_names_match_the_abi():
+    from nvfp4_block_scaled_group_amd import binding
+    for name in _declared():
+        assert name in binding.EXPORTS
+        if name != "nvfp4_group_strerror":
+            assert callable(getattr(binding, name))
+
+
+def test_strerror(lib):
+    lib.nvfp4_group_strerror.restype = ctypes.c_char_p
+    lib.nvfp4_group_strerror.argtypes = [ctypes.c_int]
+    assert lib.nvfp4_group_strerror(0) == b"ok"
+    for st in (-1, -2, -3, -4):
+        assert lib.nvfp4_group_strerror(st) != b"unknown status"
+    assert lib.nvfp4_group_strerror(7) == b"unknown status"
+
+
+def _amax(lib, x, m, k, splits, row=None, col=None):
+    f = lib.nvfp4_group_amax
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    sp = (ctypes.c_int64 * len(splits))(*splits) if splits is not None else None
+    return f(x, m, k, len(splits) if splits is not None else 0, sp, row, col, None)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails a host check first
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 256, 15, [256]), -1),            # k not a multiple of 16
+    ((FAKE, 256, 0, [256]), -1),             # k = 0
+    ((None, 256, 32, [256]), -1),            # NULL x with rows
+    ((FAKE, -128, 32, [128]), -1),           # negative rows
+    ((FAKE, 256, 32, []), -1),               # no experts
+    ((FAKE, 256, 32, [100, 156]), -2),       # split not a multiple of 128
+    ((FAKE, 256, 32, [128, 0]), -2),         # splits do not sum to sum_m
+    ((FAKE, 256, 32, [-128, 384]), -2),      # negative split
+    ((FAKE + 2, 256, 32, [256]), -3),        # misaligned x
+])
+def test_host_argument_checks(lib, args, status):
+    x, m, k, splits = args
+    assert _amax(lib, x, m, k, splits, FAKE, FAKE) == status
+
+
+def test_too_many_host_experts(lib):
+    assert _amax(lib, FAKE, 0, 32, [0] * 513, FAKE, FAKE) == -1
+
+
+def test_cast_direction_checks(lib):
+    f = lib.nvfp4_group_cast
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p] + \
+        [ctypes.c_void_p] * 7
+    sp = (ctypes.c_int64 * 1)(128)
+    # rowwise data without its scale / amax
+    assert f(FAKE, 128, 32, 1, sp, None, None, FAKE, None, None, None, None) == -1
+    assert f(FAKE, 128, 32, 1, sp, None, None, FAKE, FAKE, None, None, None) == -1
+    # columnwise data without col_amax
+    assert f(FAKE, 128, 32, 1, sp, FAKE, None, None, None, FAKE, FAKE, None) == -1
+    # misaligned output
+    assert f(FAKE, 128, 32, 1, sp, FAKE, None, FAKE + 4, FAKE, None, None, None) == -3
+
+
+def test_graphsafe_static_checks(lib):
+    f = lib.nvfp4_group_amax_graphsafe
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 5
+    assert f(FAKE, 256, 32, 2, None, FAKE, FAKE, FAKE, None) == -1        # no device offsets
+    assert f(FAKE, 256, 32, 2, FAKE, FAKE, FAKE, None, None) == -1        # no status word
+    assert f(FAKE, 200, 32, 2, FAKE, FAKE, FAKE, FAKE, None) == -1        # capacity not %128
+    assert f(FAKE, 256, 32, 0, FAKE, FAKE, FAKE, FAKE, None) == -1        # no experts
+    assert f(FAKE, 256, 32, 5000, FAKE, FAKE, FAKE, FAKE, None) == -1     # too many experts
