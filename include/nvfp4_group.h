@@ -64,8 +64,12 @@ extern "C" {
 #define NVFP4G_EALIGN (-3)  /* x or an output not suitably aligned */
 #define NVFP4G_EHIP (-4)    /* HIP launch/runtime error */
 
-/* Largest expert count of the host-split calls (the splits travel in the
- * kernel arguments) and of the graph-safe calls. */
+/* Size limits: K <= 2^22 columns and at most 2^24 rows (sum_m, or
+ * m_capacity); larger calls return NVFP4G_EINVAL.  Largest expert count of
+ * the host-split calls (the splits travel in the kernel arguments) and of the
+ * graph-safe calls. */
+#define NVFP4G_MAX_K (1 << 22)
+#define NVFP4G_MAX_ROWS (1 << 24)
 #define NVFP4G_MAX_EXPERTS_HOST 512
 #define NVFP4G_MAX_EXPERTS_DEVICE 4096
 

@@ -121,6 +121,35 @@ __device__ __forceinline__ uint32_t dpp_hmirror(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
 }
 
+// gfx950 cross-row swaps: permlane32_swap(a, b) exchanges lanes 32..63 of a
+// with lanes 0..31 of b; permlane16_swap(a, b) exchanges the odd 16-lane rows
+// of a with the even rows of b.  The max of the two results is the max over
+// lane pairs l, l^32 (resp. l, l^16) of a in the lower half (even rows) and of
+// b in the upper half (odd rows).
+__device__ __forceinline__ uint32_t swap32_max(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return pkmax(r[0], r[1]);
+}
+__device__ __forceinline__ uint32_t swap16_max(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  return pkmax(r[0], r[1]);
+}
+
+// Reduce-scatter of 8 packed values over the 64 lanes of a wave: returns, in
+// every lane, the max over all lanes of value[lane >> 3].
+__device__ __forceinline__ uint32_t wave_reduce_scatter8(const uint32_t (&v)[8], int lane) {
+  uint32_t n[4], m[2];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) n[p] = swap32_max(v[p], v[p + 4]);  // value p + 4*bit5
+#pragma unroll
+  for (int q = 0; q < 2; ++q) m[q] = swap16_max(n[q], n[q + 2]);  // + 2*bit4
+  const bool b3 = (lane >> 3) & 1;                                  // + bit3
+  uint32_t r = pkmax(b3 ? m[1] : m[0], swap8(b3 ? m[0] : m[1]));
+  r = pkmax(r, dpp_x1(r));
+  r = pkmax(r, dpp_x2(r));
+  return pkmax(r, dpp_hmirror(r));
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -156,6 +185,42 @@ __device__ __forceinline__ uint32_t block_scale(float b, float s, float* m) {
   return S;
 }
 
+// Same step with fewer operations, for line scales s >= 2^-112 (line amax of
+// about 2^-100.6 or more), given ys = 1/s (correctly rounded, once per line):
+//   u = b/6 as q0 = b*RN(1/6) plus one fused residual correction,
+//   t = u/s as t0 = u*ys plus one fused residual correction,
+//   m = 1/d as the hardware reciprocal plus one Newton step.
+// Over every pair of bf16 values b <= A with A >= 2^-102 this gives the same
+// E4M3 code, and (for A >= 2^-105) the same m bits, as the correctly rounded
+// divisions above; smaller lines take the exact path.
+constexpr float kFastMinLineScale = 0x1p-112f;
+
+__device__ __forceinline__ uint32_t block_scale_fast(float b, float s, float ys, float* m) {
+  const float r6 = 0x1.555556p-3f;  // RN(1/6)
+  const float q0 = b * r6;
+  const float u = __builtin_fmaf(__builtin_fmaf(-6.0f, q0, b), r6, q0);
+  const float t0 = u * ys;
+  const float t = __builtin_fmaf(__builtin_fmaf(-s, t0, u), ys, t0);
+  const uint32_t S = e4m3_code(t);
+  const float d = e4m3_value(S) * s;
+  const float y0 = __builtin_amdgcn_rcpf(d);
+  const float y1 = __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
+  *m = (d == 0.0f) ? 0.0f : fminf(y1, FLT_MAX);
+  return S;
+}
+
+__device__ __forceinline__ uint32_t block_step(float b, float s, float ys, float* m) {
+  if (s >= kFastMinLineScale) return block_scale_fast(b, s, ys, m);
+  return block_scale(b, s, m);
+}
+
+// Hardware FP4 conversion (gfx950): two fp32 values -> one E2M1x2 byte
+// (first value in the low nibble) placed at byte SEL of `old`.  With scale
+// 1.0 it rounds to nearest (ties to the even code), saturates at +-6 and
+// keeps the sign of zero: it equals e2m1_code below on every non-NaN fp32
+// input.
+#define FP4X2(old, a, b, SEL) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (SEL))
+
 // 4-bit E2M1 code of v: sign bit of v, magnitude nearest on
 // {0, .5, 1, 1.5, 2, 3, 4, 6} with ties to the even code, saturating.
 // |v| >= 1: round the fp32 mantissa to 1 bit; the code is then the fp32
@@ -176,9 +241,24 @@ __device__ __forceinline__ uint32_t enc_pair(uint32_t w, float m) {
   return e2m1_code(bf16lo(w) * m) | (e2m1_code(bf16hi(w) * m) << 4);
 }
 
-__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor (gfx9 layout: 32-bit data format word) over `base`.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
+// Offset of a lane that must not touch memory: beyond the descriptor range.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache policy bits: streaming (non-temporal) loads of x; plain stores.
+constexpr int kLoadStream = 2;
+#ifndef NVFP4G_STORE_AUX
+#define NVFP4G_STORE_AUX 0
+#endif
+constexpr int kStoreAux = NVFP4G_STORE_AUX;
 
 // ------------------------------------------------------------------ kernels
 
@@ -195,175 +275,311 @@ __global__ __launch_bounds__(kThreads) void amax_init_kernel(
   }
 }
 
-// Grouped amax: grid (row tiles, column chunks).
-__global__ __launch_bounds__(kThreads) void group_amax_kernel(
-    const uint16_t* __restrict__ x, int64_t k, Routing R,
-    uint32_t* __restrict__ row_amax, uint32_t* __restrict__ col_amax) {
-  __shared__ uint32_t red[4][64];
-  if (!routing_ok(R)) return;
-  const int32_t total = route_end(R, R.num_experts - 1);
-  const int32_t row0 = (int32_t)blockIdx.x * kTileRows;
-  if (row0 >= total) return;
-  int32_t rbeg, rend;
-  const int e = find_expert(R, row0, &rbeg, &rend);
+// Work decomposition shared by both kernels.  The (sum_M x K) buffer is cut
+// into strips of kStrip consecutive 128-row sub-tiles by chunks of 256
+// columns; a workgroup walks one strip top to bottom, so the transposed
+// lines it writes are contiguous over its whole strip, and the column amax
+// of a strip needs one flush per expert it touches.  Workgroups are
+// dispatched round-robin over the 8 XCDs (each with its own L2), so the
+// linear block id is remapped to give each XCD a contiguous range of strips:
+// vertically adjacent strips, which write the two halves of shared output
+// lines, then go through the same L2.
+#ifndef NVFP4G_STRIP
+#define NVFP4G_STRIP 1
+#endif
+constexpr int kStrip = NVFP4G_STRIP;
+constexpr int kNumXcd = 8;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rb = lane & 7, cg = lane >> 3;
-  const int64_t col = (int64_t)blockIdx.y * kTileCols + wave * 64 + cg * 8;
-  const bool active = col < k;
+struct TileCoord {
+  uint32_t strip, chunk;
+};
 
-  uint32_t v[16][4];
-  const uint16_t* p = x + ((int64_t)row0 + 16 * rb) * k + col;
+__device__ __forceinline__ TileCoord tile_coord(uint32_t nstrips) {
+  const uint32_t nb = gridDim.x, L = blockIdx.x;
+  const uint32_t xcd = L % kNumXcd, q = nb / kNumXcd, r = nb % kNumXcd;
+  const uint32_t lt = xcd * q + min(xcd, r) + L / kNumXcd;  // a permutation of 0..nb-1
+  return TileCoord{lt % nstrips, lt / nstrips};
+}
+
+// Loads the lane's 16 rows x 8 columns (16 x 16 bytes) of a 128 x 256 tile
+// whose first element is `tile`; `vo` is the lane's byte offset (or
+// kOutOfRange), row i adds i*K*2 bytes as a scalar offset.
+__device__ __forceinline__ void load_tile(const uint16_t* tile, uint32_t ku, uint32_t vo,
+                                          uint32_t (&v)[16][4]) {
+  const rsrc_t xr = make_rsrc(tile);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    uint4 q = active ? ldg16(p + i * k) : make_uint4(0, 0, 0, 0);
-    v[i][0] = q.x & 0x7FFF7FFFu; v[i][1] = q.y & 0x7FFF7FFFu;
-    v[i][2] = q.z & 0x7FFF7FFFu; v[i][3] = q.w & 0x7FFF7FFFu;
-  }
-
-  if (row_amax) {
-    // per row pair (2p, 2p+1): low half = row 2p, high half = row 2p+1
-    uint32_t rp[8];
-#pragma unroll
-    for (int pr = 0; pr < 8; ++pr) {
-      const uint32_t a = pkmax(pkmax(v[2 * pr][0], v[2 * pr][1]), pkmax(v[2 * pr][2], v[2 * pr][3]));
-      const uint32_t b = pkmax(pkmax(v[2 * pr + 1][0], v[2 * pr + 1][1]),
-                               pkmax(v[2 * pr + 1][2], v[2 * pr + 1][3]));
-      const uint32_t lo = (a & 0xFFFFu) | (b << 16);
-      const uint32_t hi = (a >> 16) | (b & 0xFFFF0000u);
-      uint32_t r = pkmax(lo, hi);
-      r = pkmax(r, swap8(r));
-      r = pkmax(r, (uint32_t)__shfl_xor((int)r, 16));
-      r = pkmax(r, (uint32_t)__shfl_xor((int)r, 32));
-      rp[pr] = r;
-    }
-    if (cg == 0) {
-#pragma unroll
-      for (int pr = 0; pr < 8; ++pr) red[wave][rb * 8 + pr] = rp[pr];
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const int t = threadIdx.x;
-      const uint32_t r = pkmax(pkmax(red[0][t], red[1][t]), pkmax(red[2][t], red[3][t]));
-      const int64_t row = (int64_t)row0 + 16 * (t >> 3) + 2 * (t & 7);
-      atomicMax(row_amax + row, r << 16);
-      atomicMax(row_amax + row + 1, r & 0xFFFF0000u);
-    }
-  }
-
-  if (col_amax) {
-    uint32_t c[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t m = v[0][j];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) m = pkmax(m, v[i][j]);
-      m = pkmax(m, dpp_x1(m));
-      m = pkmax(m, dpp_x2(m));
-      m = pkmax(m, dpp_hmirror(m));
-      c[j] = m;
-    }
-    // lanes rb = 0..3 each publish one column pair
-    if (active && rb < 4) {
-      const uint32_t m = rb == 0 ? c[0] : rb == 1 ? c[1] : rb == 2 ? c[2] : c[3];
-      uint32_t* dst = col_amax + (int64_t)e * k + col + 2 * rb;
-      atomicMax(dst, m << 16);
-      atomicMax(dst + 1, m & 0xFFFF0000u);
-    }
+    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, vo, (uint32_t)i * ku * 2u, kLoadStream);
+    v[i][0] = q.x; v[i][1] = q.y; v[i][2] = q.z; v[i][3] = q.w;
   }
 }
 
-// Grouped cast: grid (row tiles, column chunks); rowwise and/or columnwise.
-__global__ __launch_bounds__(kThreads) void group_cast_kernel(
+// Grouped amax, persistent: a grid of G workgroups, workgroup g walks the
+// contiguous range [g*T/G, (g+1)*T/G) of the T tiles of 64 rows x 512
+// columns, ordered row tile fastest within each 512-column chunk (so a
+// workgroup mostly walks down one chunk).  A wave covers 16 rows x 512
+// columns: lane L holds columns 8L..8L+7 of the wave's 16 rows, so each wave
+// load reads 1 KB of one row.  The next tile's loads are issued before the
+// current tile is reduced.  Column maxima stay in registers while the
+// (expert, chunk) pair is unchanged and are flushed with one atomic max per
+// column when it changes; each row gets one atomic max per 512-column chunk.
+constexpr int kAmaxRows = 64;
+constexpr int kAmaxCols = 512;
+
+struct AmaxTile {
+  int32_t row0;   // first row
+  int32_t chunk;  // 512-column chunk
+};
+
+__device__ __forceinline__ void amax_load(const uint16_t* x, uint32_t ku, int32_t row0, int32_t chunk,
+                                          uint32_t lane_off, uint32_t (&v)[16][4]) {
+  const rsrc_t xr = make_rsrc(x + (int64_t)row0 * ku + (int64_t)chunk * kAmaxCols);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, lane_off, (uint32_t)i * ku * 2u, kLoadStream);
+    v[i][0] = q.x; v[i][1] = q.y; v[i][2] = q.z; v[i][3] = q.w;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void group_amax_kernel(
     const uint16_t* __restrict__ x, int64_t k, Routing R,
+    uint32_t* __restrict__ row_amax, uint32_t* __restrict__ col_amax) {
+  __shared__ uint32_t l_col[4][kAmaxCols / 2];  // per wave, column pairs
+  if (!routing_ok(R)) return;
+  const int32_t total = route_end(R, R.num_experts - 1);
+  const uint32_t ku = (uint32_t)k;
+  const uint32_t nchunks = (ku + kAmaxCols - 1) / kAmaxCols;
+  const uint32_t nrt = (uint32_t)total / kAmaxRows;  // total is a multiple of 128
+  const uint32_t T = nrt * nchunks;
+  const uint32_t t_begin = (uint32_t)(((uint64_t)blockIdx.x * T) / gridDim.x);
+  const uint32_t t_end = (uint32_t)(((uint64_t)(blockIdx.x + 1) * T) / gridDim.x);
+  if (t_begin >= t_end) return;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t lcol = lane * 8;  // within the chunk
+  auto tile_of = [&](uint32_t t) { return AmaxTile{(int32_t)(t % nrt) * kAmaxRows, (int32_t)(t / nrt)}; };
+  auto lane_off = [&](int32_t chunk) -> uint32_t {
+    return (uint32_t)chunk * kAmaxCols + lcol < ku ? (16u * wave * ku + lcol) * 2u : kOutOfRange;
+  };
+
+  uint32_t c[4] = {0, 0, 0, 0};  // running column maxima (2 bf16 columns per word)
+  int key_e = -1, key_chunk = -1;
+
+  auto flush_cols = [&]() {
+    __syncthreads();  // previous readers of l_col are done
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l_col[wave][lane * 4 + j] = c[j];
+    __syncthreads();
+    const int p = threadIdx.x;  // one column pair per thread
+    const uint32_t m = pkmax(pkmax(l_col[0][p], l_col[1][p]), pkmax(l_col[2][p], l_col[3][p]));
+    const uint32_t col = (uint32_t)key_chunk * kAmaxCols + 2 * p;
+    if (col < ku) {
+      uint32_t* dst = col_amax + (int64_t)key_e * k + col;
+      atomicMax(dst, m << 16);
+      atomicMax(dst + 1, m & 0xFFFF0000u);
+    }
+  };
+
+  uint32_t va[16][4], vb[16][4];
+  AmaxTile cur = tile_of(t_begin);
+  amax_load(x, ku, cur.row0, cur.chunk, lane_off(cur.chunk), va);
+
+  auto process = [&](uint32_t (&v)[16][4], AmaxTile tl) {
+    int32_t rbeg, rend;
+    const int e = find_expert(R, tl.row0, &rbeg, &rend);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[i][j] &= 0x7FFF7FFFu;
+    if (col_amax) {
+      if (e != key_e || tl.chunk != key_chunk) {
+        if (key_e >= 0) flush_cols();
+        c[0] = c[1] = c[2] = c[3] = 0;
+        key_e = e;
+        key_chunk = tl.chunk;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[j] = pkmax(c[j], v[i][j]);
+    }
+    if (row_amax) {
+      // rows (2p, 2p+1) of the wave packed in one word, p = 0..7
+      uint32_t rp[8];
+#pragma unroll
+      for (int pr = 0; pr < 8; ++pr) {
+        const uint32_t a = pkmax(pkmax(v[2 * pr][0], v[2 * pr][1]), pkmax(v[2 * pr][2], v[2 * pr][3]));
+        const uint32_t b = pkmax(pkmax(v[2 * pr + 1][0], v[2 * pr + 1][1]),
+                                 pkmax(v[2 * pr + 1][2], v[2 * pr + 1][3]));
+        rp[pr] = pkmax((a & 0xFFFFu) | (b << 16), (a >> 16) | (b & 0xFFFF0000u));
+      }
+      const uint32_t g = wave_reduce_scatter8(rp, lane);  // pair lane/8, all 64 lanes reduced
+      if ((lane & 7) == 0) {
+        const int64_t row = (int64_t)tl.row0 + 16 * wave + 2 * (lane >> 3);
+        atomicMax(row_amax + row, g << 16);
+        atomicMax(row_amax + row + 1, g & 0xFFFF0000u);
+      }
+    }
+  };
+
+#pragma unroll 1
+  for (uint32_t t = t_begin; t < t_end; t += 2) {
+    AmaxTile nxt = tile_of(t + 1);
+    if (t + 1 < t_end) amax_load(x, ku, nxt.row0, nxt.chunk, lane_off(nxt.chunk), vb);
+    process(va, cur);
+    if (t + 1 >= t_end) break;
+    cur = tile_of(t + 2);
+    if (t + 2 < t_end) amax_load(x, ku, cur.row0, cur.chunk, lane_off(cur.chunk), va);
+    process(vb, nxt);
+  }
+  if (col_amax && key_e >= 0) flush_cols();
+}
+
+// Grouped cast over one strip x 256 columns; rowwise and/or columnwise.
+//
+// Addressing: every tensor is reached through a raw buffer descriptor whose
+// base is the tile's first element, a per-lane 32-bit offset and a scalar
+// per-row (or per-column) offset, so no per-store 64-bit address arithmetic
+// is done on the vector ALUs.  Lanes whose columns lie beyond K get an offset
+// past the descriptor's range: their loads return 0 and their stores are
+// dropped by the hardware range check.
+__global__ __launch_bounds__(kThreads) void group_cast_kernel(
+    const uint16_t* __restrict__ x, int64_t k, Routing R, uint32_t nstrips,
     const float* __restrict__ row_amax, const float* __restrict__ col_amax,
     uint8_t* __restrict__ row_data, uint8_t* __restrict__ row_scale,
     uint8_t* __restrict__ col_data, uint8_t* __restrict__ col_scale) {
-  __shared__ float s_row[kTileRows];
-  __shared__ float s_col[kTileCols];
+  __shared__ float2 l_row[kTileRows];                   // (s, 1/s) per row of the tile
+  __shared__ float2 l_col[kTileCols];                   // (s, 1/s) per column of the tile
+  __shared__ uint32_t l_rs[kTileRows][kTileCols / 64];  // row scales, 16 per row
+  __shared__ uint32_t l_cs[kTileCols][2];               // column scales, 8 per column
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
-  const int32_t row0 = (int32_t)blockIdx.x * kTileRows;
-  if (row0 >= total) return;
-  int32_t rbeg, rend;
-  const int e = find_expert(R, row0, &rbeg, &rend);
-  const int64_t me = rend - rbeg;
+  const TileCoord tc = tile_coord(nstrips);
+  const int32_t strip_row0 = (int32_t)tc.strip * kStrip * kTileRows;
+  if (strip_row0 >= total) return;
+  const int64_t col_base = (int64_t)tc.chunk * kTileCols;
+  const uint32_t ncols = (uint32_t)min<int64_t>(k - col_base, kTileCols);
+  const uint32_t ku = (uint32_t)k;
 
   const int tid = threadIdx.x;
-  const int64_t col_base = (int64_t)blockIdx.y * kTileCols;
-  // line scales s = A / (6 * 448), once per line per tile
-  if (row_data && tid < kTileRows) s_row[tid] = row_amax[row0 + tid] / 2688.0f;
-  if (col_data) {
-    const int64_t c = col_base + tid;
-    s_col[tid] = c < k ? col_amax[(int64_t)e * k + c] / 2688.0f : 0.0f;
-  }
-  __syncthreads();
-
   const int wave = tid >> 6, lane = tid & 63;
   const int rb = lane & 7, cg = lane >> 3;
-  const int64_t col = col_base + wave * 64 + cg * 8;
-  const bool active = col < k;
+  const uint32_t lcol = wave * 64 + cg * 8;  // lane's first column within the tile
+  const bool active = lcol < ncols;
+  const uint32_t vo_x = active ? (16u * rb * ku + lcol) * 2u : kOutOfRange;
+  int e_cur = -1;
 
-  uint32_t v[16][4];
-  const uint16_t* p = x + ((int64_t)row0 + 16 * rb) * k + col;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint4 q = active ? ldg16(p + i * k) : make_uint4(0, 0, 0, 0);
-    v[i][0] = q.x; v[i][1] = q.y; v[i][2] = q.z; v[i][3] = q.w;
-  }
+#pragma unroll 1
+  for (int h = 0; h < kStrip; ++h) {
+    const int32_t row0 = strip_row0 + h * kTileRows;
+    if (row0 >= total) break;
+    int32_t rbeg, rend;
+    const int e = find_expert(R, row0, &rbeg, &rend);
+    const uint32_t me = (uint32_t)(rend - rbeg);
 
-  if (row_data) {
+    uint32_t v[16][4];
+    load_tile(x + (int64_t)row0 * k + col_base, ku, vo_x, v);
+    if (h) __syncthreads();  // the previous sub-tile is done with the LDS tables
+    if (row_data && tid < kTileRows) {
+      const float s = row_amax[row0 + tid] / 2688.0f;
+      l_row[tid] = make_float2(s, 1.0f / s);
+    }
+    if (col_data && e != e_cur) {
+      const float s = (uint32_t)tid < ncols ? col_amax[(int64_t)e * k + col_base + tid] / 2688.0f : 0.0f;
+      l_col[tid] = make_float2(s, 1.0f / s);
+    }
+    e_cur = e;
+    __syncthreads();
+
+    if (row_data) {
+      // block amax of each of the lane's 16 rows over 16 columns (own 8 + lane^8)
+      uint32_t b16[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t a = pkmax(pkmax(v[i][0] & 0x7FFF7FFFu, v[i][1] & 0x7FFF7FFFu),
-                               pkmax(v[i][2] & 0x7FFF7FFFu, v[i][3] & 0x7FFF7FFFu));
-      uint32_t b16 = hmax(a);
-      b16 = max(b16, swap8(b16));
-      float m;
-      const uint32_t S = block_scale(__uint_as_float(b16 << 16), s_row[16 * rb + i], &m);
-      const uint32_t packed = enc_pair(v[i][0], m) | (enc_pair(v[i][1], m) << 8) |
-                              (enc_pair(v[i][2], m) << 16) | (enc_pair(v[i][3], m) << 24);
-      const int64_t r = (int64_t)row0 + 16 * rb + i;
-      if (active) {
-        *reinterpret_cast<uint32_t*>(row_data + r * (k / 2) + col / 2) = packed;
-        if (!(cg & 1)) row_scale[r * (k / 16) + col / 16] = (uint8_t)S;
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t a = pkmax(pkmax(v[i][0] & 0x7FFF7FFFu, v[i][1] & 0x7FFF7FFFu),
+                                 pkmax(v[i][2] & 0x7FFF7FFFu, v[i][3] & 0x7FFF7FFFu));
+        b16[i] = hmax(a);
+        b16[i] = max(b16[i], swap8(b16[i]));
+      }
+      // the lane pair shares each block: the even lane derives the scales of
+      // rows 0..7, the odd lane those of rows 8..15, then they swap
+      const bool odd = cg & 1;
+      float mrow[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ri = odd ? 8 + i : i;
+        const float2 sl = l_row[16 * rb + ri];
+        float m;
+        const uint32_t S = block_step(__uint_as_float((odd ? b16[8 + i] : b16[i]) << 16), sl.x, sl.y, &m);
+        const float mo = __uint_as_float(swap8(__float_as_uint(m)));
+        mrow[i] = odd ? mo : m;
+        mrow[8 + i] = odd ? m : mo;
+        reinterpret_cast<uint8_t*>(&l_rs[16 * rb + ri][0])[wave * 4 + (cg >> 1)] = (uint8_t)S;
+      }
+      const rsrc_t rd = make_rsrc(row_data + (int64_t)row0 * (k / 2) + col_base / 2);
+      const uint32_t vo = active ? 16u * rb * (ku / 2) + lcol / 2 : kOutOfRange;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float m = mrow[i];
+        uint32_t packed = 0;
+        packed = FP4X2(packed, bf16lo(v[i][0]) * m, bf16hi(v[i][0]) * m, 0);
+        packed = FP4X2(packed, bf16lo(v[i][1]) * m, bf16hi(v[i][1]) * m, 1);
+        packed = FP4X2(packed, bf16lo(v[i][2]) * m, bf16hi(v[i][2]) * m, 2);
+        packed = FP4X2(packed, bf16lo(v[i][3]) * m, bf16hi(v[i][3]) * m, 3);
+        __builtin_amdgcn_raw_buffer_store_b32(packed, rd, vo, (uint32_t)i * (ku / 2), kStoreAux);
       }
     }
-  }
 
-  if (col_data) {
-    uint8_t* cd = col_data + k * (int64_t)rbeg / 2;
-    uint8_t* cs = col_scale + k * (int64_t)rbeg / 16;
-    const int64_t rofs = (int64_t)row0 - rbeg + 16 * rb;  // row within expert
+    if (col_data) {
+      const rsrc_t cd = make_rsrc(col_data + k * (int64_t)rbeg / 2 + col_base * (me / 2) + (row0 - rbeg) / 2);
+      const uint32_t vo = active ? lcol * (me / 2) + 8u * rb : kOutOfRange;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t mx = 0;
+      for (int j = 0; j < 8; ++j) {
+        uint32_t mx = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = pkmax(mx, v[i][j >> 1] & 0x7FFF7FFFu);
-      const uint32_t b16 = (j & 1) ? (mx >> 16) : (mx & 0xFFFFu);
-      float m;
-      const uint32_t S = block_scale(__uint_as_float(b16 << 16), s_col[wave * 64 + cg * 8 + j], &m);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t w = v[i][j >> 1];
-        lo |= e2m1_code(((j & 1) ? bf16hi(w) : bf16lo(w)) * m) << (4 * i);
+        for (int i = 0; i < 16; ++i) mx = pkmax(mx, v[i][j >> 1] & 0x7FFF7FFFu);
+        const uint32_t b16 = (j & 1) ? (mx >> 16) : (mx & 0xFFFFu);
+        const float2 sl = l_col[lcol + j];
+        float m;
+        const uint32_t S = block_step(__uint_as_float(b16 << 16), sl.x, sl.y, &m);
+        reinterpret_cast<uint8_t*>(&l_cs[lcol + j][0])[rb] = (uint8_t)S;
+#define XCOL(i) (((j & 1) ? bf16hi(v[i][j >> 1]) : bf16lo(v[i][j >> 1])) * m)
+        uint32_t lo = 0, hi = 0;
+        lo = FP4X2(lo, XCOL(0), XCOL(1), 0);
+        lo = FP4X2(lo, XCOL(2), XCOL(3), 1);
+        lo = FP4X2(lo, XCOL(4), XCOL(5), 2);
+        lo = FP4X2(lo, XCOL(6), XCOL(7), 3);
+        hi = FP4X2(hi, XCOL(8), XCOL(9), 0);
+        hi = FP4X2(hi, XCOL(10), XCOL(11), 1);
+        hi = FP4X2(hi, XCOL(12), XCOL(13), 2);
+        hi = FP4X2(hi, XCOL(14), XCOL(15), 3);
+#undef XCOL
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, cd, vo, (uint32_t)j * (me / 2), kStoreAux);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t w = v[8 + i][j >> 1];
-        hi |= e2m1_code(((j & 1) ? bf16hi(w) : bf16lo(w)) * m) << (4 * i);
+    }
+
+    // scales: staged in LDS, then one wide store per row / per column
+    __syncthreads();
+    if (row_data && tid < kTileRows) {
+      uint8_t* dst = row_scale + ((int64_t)row0 + tid) * (k / 16) + col_base / 16;
+      if (ncols == kTileCols && (k & 255) == 0) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&l_rs[tid][0]);
+      } else {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(&l_rs[tid][0]);
+        for (uint32_t b = 0; b < ncols / 16; ++b) dst[b] = src[b];
       }
-      if (active) {
-        const int64_t c = col + j;
-        *reinterpret_cast<uint2*>(cd + c * (me / 2) + rofs / 2) = make_uint2(lo, hi);
-        cs[c * (me / 16) + rofs / 16] = (uint8_t)S;
-      }
+    }
+    if (col_data && (uint32_t)tid < ncols) {
+      uint8_t* dst = col_scale + k * (int64_t)rbeg / 16 + (col_base + tid) * (int64_t)(me / 16) + (row0 - rbeg) / 16;
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&l_cs[tid][0]);
     }
   }
 }
 
 // ------------------------------------------------------------- host side
+
+constexpr int64_t kMaxK = NVFP4G_MAX_K;
+constexpr int64_t kMaxRows = NVFP4G_MAX_ROWS;
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -373,8 +589,9 @@ int hip_status() {
 
 // Common static checks; fills R (all but the offsets).
 int check_common(const uint16_t* x, int64_t rows, int64_t k, int32_t E, Routing* R) {
-  if (k <= 0 || k % 16 != 0 || k > (int64_t)1 << 30) return NVFP4G_EINVAL;
-  if (rows < 0 || rows > INT32_MAX - kTileRows) return NVFP4G_EINVAL;
+  // size limits keep every per-lane and per-row buffer offset below 2^31
+  if (k <= 0 || k % 16 != 0 || k > kMaxK) return NVFP4G_EINVAL;
+  if (rows < 0 || rows > kMaxRows) return NVFP4G_EINVAL;
   if (rows > 0 && x == nullptr) return NVFP4G_EINVAL;
   if (!aligned(x, 16)) return NVFP4G_EALIGN;
   R->num_experts = E;
@@ -408,8 +625,22 @@ int check_cast_outputs(const float* row_amax, const float* col_amax, const uint8
   return NVFP4G_OK;
 }
 
+// Number of strips (kStrip x 128 rows) covering `rows` rows, and the 1-D
+// grid of strips x 256-column chunks.
+uint32_t num_strips(int64_t rows) {
+  return (uint32_t)((rows + kStrip * kTileRows - 1) / (kStrip * kTileRows));
+}
+// Persistent amax grid: enough resident workgroups to cover the device
+// (at most the number of 64 x 512 tiles of the buffers).
+#ifndef NVFP4G_AMAX_WGS
+#define NVFP4G_AMAX_WGS 768
+#endif
+unsigned amax_grid(int64_t rows, int64_t k) {
+  const int64_t tiles = (rows / kAmaxRows) * ((k + kAmaxCols - 1) / kAmaxCols);
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(tiles, NVFP4G_AMAX_WGS));
+}
 dim3 tile_grid(int64_t rows, int64_t k) {
-  return dim3((unsigned)((rows + kTileRows - 1) / kTileRows), (unsigned)((k + kTileCols - 1) / kTileCols));
+  return dim3(num_strips(rows) * (unsigned)((k + kTileCols - 1) / kTileCols));
 }
 
 int launch_amax(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, float* row_amax,
@@ -419,7 +650,7 @@ int launch_amax(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, fl
   const unsigned init_blocks = (unsigned)std::min<int64_t>(std::max<int64_t>((n + kThreads - 1) / kThreads, 1), 4096);
   hipLaunchKernelGGL(amax_init_kernel, dim3(init_blocks), dim3(kThreads), 0, st, R, k, row_amax, col_amax);
   if (rows > 0)
-    hipLaunchKernelGGL(group_amax_kernel, tile_grid(rows, k), dim3(kThreads), 0, st, x, k, R,
+    hipLaunchKernelGGL(group_amax_kernel, dim3(amax_grid(rows, k)), dim3(kThreads), 0, st, x, k, R,
                        reinterpret_cast<uint32_t*>(row_amax), reinterpret_cast<uint32_t*>(col_amax));
   return hip_status();
 }
@@ -428,7 +659,7 @@ int launch_cast(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, co
                 const float* col_amax, uint8_t* row_data, uint8_t* row_scale, uint8_t* col_data,
                 uint8_t* col_scale, hipStream_t st) {
   if ((!row_data && !col_data) || rows == 0) return NVFP4G_OK;
-  hipLaunchKernelGGL(group_cast_kernel, tile_grid(rows, k), dim3(kThreads), 0, st, x, k, R, row_amax,
+  hipLaunchKernelGGL(group_cast_kernel, tile_grid(rows, k), dim3(kThreads), 0, st, x, k, R, num_strips(rows), row_amax,
                      col_amax, row_data, row_scale, col_data, col_scale);
   return hip_status();
 }
