@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "grouped NVFP4 amax+cast HBM GB/s (bytes in+out) and % of MI355X peak BW"
+TRAFFIC_FILE = "profiles/group_cast_kernel-deepseek_share_e32_k7168_m65536.md"
 
 
 def algorithmic_bytes(sum_m: int, k: int, E: int, rowwise: bool, columnwise: bool) -> dict:
@@ -70,6 +71,9 @@ def main():
                     choices=["deepseek_share", "down_proj", "outliers", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph-replays", type=int, default=100)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (3 times, untimed) so that a "
+                         "rocprofv3 --pmc run can scale FETCH_SIZE / WRITE_SIZE by a copy of known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -119,6 +123,12 @@ def main():
     cast_gbs = nbytes["cast_kernel"] / (cast_ms * 1e-3) / 1e9
     amax_gbs = nbytes["amax_kernel"] / (amax_ms * 1e-3) / 1e9
 
+    # HBM bytes per launch of the cast kernel from the committed FETCH_SIZE /
+    # WRITE_SIZE summary, only while the HIP source is the one it was taken on
+    from nvfp4_block_scaled_group_amd import profiling
+    traffic = (profiling.load_traffic(os.path.join(ROOT, TRAFFIC_FILE), "group_cast_kernel")
+               if args.workload == "deepseek_share" else None)
+
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -132,12 +142,22 @@ def main():
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "kernel": "group_cast_kernel", "achieved": round(cast_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(cast_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_us": round(cast_ms * 1e3, 2),
+                     "traffic": traffic["bytes"] if traffic else None,
+                     "traffic_source": TRAFFIC_FILE if traffic else None,
+                     "avg_us": round(cast_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": nbytes["cast_kernel"]},
         "kernels": {"amax (init + group_amax_kernel)": {"avg_us": round(amax_ms * 1e3, 2),
                                                         "GBps": round(amax_gbs, 2)},
                     "group_cast_kernel": {"avg_us": round(cast_ms * 1e3, 2), "GBps": round(cast_gbs, 2)}},
     }
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if args.workload == "deepseek_share" and args.graph_replays > 0:
         result["graph_replay"] = graph_replay(B, synth, torch, dev, args.graph_replays)

@@ -3,8 +3,8 @@
  * NVFP4 amax + cast of packed MoE expert activations/gradients on MI355X.
  *
  * What is computed (pages cited by title and section):
- *  - "[Common] Single-launch grouped row-scaled NVFP4 cast" (TransformerEngine
- *    issue 3649), Description: one grouped amax launch over the packed
+ *  - the TransformerEngine issue 3649 page (single-launch grouped
+ *    row-scaled NVFP4 cast), Description: one grouped amax launch over the packed
  *    (sum_M, K) buffer produces a rowwise [sum_M] and a columnwise
  *    [num_experts * K] amax (both directions in one pass); one grouped cast
  *    launch consumes them; each has a graph-safe twin that reads the routing
@@ -80,8 +80,8 @@ extern "C" {
 #define NVFP4G_DEV_NONMONO 2   /* offsets decrease (or the first is negative) */
 #define NVFP4G_DEV_OVERFLOW 4  /* offs[E-1] > m_capacity */
 
-/* Grouped amax ("[Common] Single-launch grouped row-scaled NVFP4 cast",
- * Description).  x: [sum_m, k] bf16; h_splits: host array of E row counts
+/* Grouped amax (TransformerEngine issue 3649 page, single-launch grouped
+ * row-scaled NVFP4 cast, Description).  x: [sum_m, k] bf16; h_splits: host array of E row counts
  * (each >= 0, a multiple of 128, summing to sum_m).  Writes
  * row_amax[r] = max_c |x[r, c]| and col_amax[e*k + c] = max over the rows of
  * expert e of |x[r, c]| (0 for an expert with no rows).  Either output may

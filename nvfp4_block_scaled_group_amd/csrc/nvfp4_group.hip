@@ -3,8 +3,8 @@
 // include/nvfp4_group.h.
 //
 // Operation (cited by page title and section):
-//  * "[Common] Single-launch grouped row-scaled NVFP4 cast" (TransformerEngine
-//    issue 3649), Description: a grouped amax over the packed (sum_M, K)
+//  * the TransformerEngine issue 3649 page (single-launch grouped
+//    row-scaled NVFP4 cast), Description: a grouped amax over the packed (sum_M, K)
 //    buffer gives rowwise [sum_M] and columnwise [num_experts*K] amax in one
 //    pass; a grouped cast consumes them; graph-safe twins read the routing
 //    from device offsets and share the device body (byte-identical output).
@@ -54,8 +54,14 @@ struct Routing {
   int32_t h_offs[NVFP4G_MAX_EXPERTS_HOST];  // host-split inclusive row ends
 };
 
+// Values that are uniform over a workgroup (routing, tile coordinates) are
+// passed through readfirstlane so the compiler keeps them, and the buffer
+// descriptors built from them, in scalar registers.
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+
 __device__ __forceinline__ int32_t route_end(const Routing& R, int e) {
-  return R.d_offs ? R.d_offs[e] : R.h_offs[e];
+  return uni(R.d_offs ? R.d_offs[e] : R.h_offs[e]);
 }
 
 // Device routing check (graph-safe calls only): every wave checks all
@@ -298,7 +304,7 @@ __device__ __forceinline__ TileCoord tile_coord(uint32_t nstrips) {
   const uint32_t nb = gridDim.x, L = blockIdx.x;
   const uint32_t xcd = L % kNumXcd, q = nb / kNumXcd, r = nb % kNumXcd;
   const uint32_t lt = xcd * q + min(xcd, r) + L / kNumXcd;  // a permutation of 0..nb-1
-  return TileCoord{lt % nstrips, lt / nstrips};
+  return TileCoord{uni(lt % nstrips), uni(lt / nstrips)};
 }
 
 // Loads the lane's 16 rows x 8 columns (16 x 16 bytes) of a 128 x 256 tile
@@ -351,13 +357,15 @@ __global__ __launch_bounds__(kThreads) void group_amax_kernel(
   const uint32_t nchunks = (ku + kAmaxCols - 1) / kAmaxCols;
   const uint32_t nrt = (uint32_t)total / kAmaxRows;  // total is a multiple of 128
   const uint32_t T = nrt * nchunks;
-  const uint32_t t_begin = (uint32_t)(((uint64_t)blockIdx.x * T) / gridDim.x);
-  const uint32_t t_end = (uint32_t)(((uint64_t)(blockIdx.x + 1) * T) / gridDim.x);
+  const uint32_t t_begin = uni((uint32_t)(((uint64_t)blockIdx.x * T) / gridDim.x));
+  const uint32_t t_end = uni((uint32_t)(((uint64_t)(blockIdx.x + 1) * T) / gridDim.x));
   if (t_begin >= t_end) return;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t lcol = lane * 8;  // within the chunk
-  auto tile_of = [&](uint32_t t) { return AmaxTile{(int32_t)(t % nrt) * kAmaxRows, (int32_t)(t / nrt)}; };
+  auto tile_of = [&](uint32_t t) {
+    return AmaxTile{(int32_t)uni(t % nrt) * kAmaxRows, (int32_t)uni(t / nrt)};
+  };
   auto lane_off = [&](int32_t chunk) -> uint32_t {
     return (uint32_t)chunk * kAmaxCols + lcol < ku ? (16u * wave * ku + lcol) * 2u : kOutOfRange;
   };
@@ -576,6 +584,90 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
   }
 }
 
+// Rowwise-only amax + cast in one pass over x (the per-row form of "Implement
+// per-token NVFP4 fprop recipe", Important Files Changed: the row amax and the
+// quantisation of the row in one go).  A wave owns whole rows: lane L holds
+// columns 512*g + 8L .. +7 for the row's segments g < NSEG (K <= 512*NSEG),
+// so each segment load reads 1 KB of the row; the row amax is a wave
+// reduction, and a 16-column block is the values of lanes 2j and 2j+1.  The
+// next row's loads are in flight while the current row is encoded.  Rows only
+// need the routed row count: expert boundaries do not affect rowwise output.
+template <int NSEG>
+__global__ __launch_bounds__(kThreads) void group_quantize_rowwise_kernel(
+    const uint16_t* __restrict__ x, int64_t k, Routing R, float* __restrict__ row_amax,
+    uint8_t* __restrict__ row_data, uint8_t* __restrict__ row_scale) {
+  if (!routing_ok(R)) return;
+  const uint32_t total = (uint32_t)route_end(R, R.num_experts - 1);
+  const uint32_t ku = (uint32_t)k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  const uint32_t w0 = blockIdx.x * (kThreads / 64) + wave;
+  uint32_t off[NSEG];  // lane's byte offset of each segment within a row (or out of range)
+#pragma unroll
+  for (int g = 0; g < NSEG; ++g) off[g] = (uint32_t)g * 512u + lane * 8u < ku ? ((uint32_t)g * 512u + lane * 8u) * 2u : kOutOfRange;
+
+  // row indices are wave-uniform: readfirstlane keeps the 64-bit row base in
+  // scalar registers, and only the small lane offsets are per lane
+  auto load_row = [&](uint32_t r, uint32_t (&v)[NSEG][4]) {
+    const rsrc_t xr = make_rsrc(x + (int64_t)__builtin_amdgcn_readfirstlane(r) * k);
+#pragma unroll
+    for (int g = 0; g < NSEG; ++g) {
+      const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, off[g], 0, kLoadStream);
+      v[g][0] = q.x; v[g][1] = q.y; v[g][2] = q.z; v[g][3] = q.w;
+    }
+  };
+  auto do_row = [&](uint32_t r, uint32_t (&v)[NSEG][4]) {
+    // row amax: lane max, then the max over the 64 lanes
+    uint32_t a = 0;
+#pragma unroll
+    for (int g = 0; g < NSEG; ++g)
+      a = pkmax(a, pkmax(pkmax(v[g][0] & 0x7FFF7FFFu, v[g][1] & 0x7FFF7FFFu),
+                         pkmax(v[g][2] & 0x7FFF7FFFu, v[g][3] & 0x7FFF7FFFu)));
+    a = hmax(a);
+    a = max(a, dpp_x1(a));
+    a = max(a, dpp_x2(a));
+    a = max(a, dpp_hmirror(a));
+    a = max(a, swap8(a));
+    a = max(a, swap32_max(a, a) & 0xFFFFu);
+    a = max(a, swap16_max(a, a) & 0xFFFFu);
+    const float A = __uint_as_float(a << 16);
+    if (lane == 0) row_amax[r] = A;
+    const float s = A / 2688.0f, ys = 1.0f / s;
+    const rsrc_t rd = make_rsrc(row_data + (int64_t)__builtin_amdgcn_readfirstlane(r) * (k / 2));
+#pragma unroll
+    for (int g = 0; g < NSEG; ++g) {
+      uint32_t b = hmax(pkmax(pkmax(v[g][0] & 0x7FFF7FFFu, v[g][1] & 0x7FFF7FFFu),
+                              pkmax(v[g][2] & 0x7FFF7FFFu, v[g][3] & 0x7FFF7FFFu)));
+      b = max(b, dpp_x1(b));  // the block is lanes 2j, 2j+1
+      float m;
+      const uint32_t S = block_step(__uint_as_float(b << 16), s, ys, &m);
+      uint32_t packed = 0;
+      packed = FP4X2(packed, bf16lo(v[g][0]) * m, bf16hi(v[g][0]) * m, 0);
+      packed = FP4X2(packed, bf16lo(v[g][1]) * m, bf16hi(v[g][1]) * m, 1);
+      packed = FP4X2(packed, bf16lo(v[g][2]) * m, bf16hi(v[g][2]) * m, 2);
+      packed = FP4X2(packed, bf16lo(v[g][3]) * m, bf16hi(v[g][3]) * m, 3);
+      const uint32_t c = (uint32_t)g * 512u + lane * 8u;
+      __builtin_amdgcn_raw_buffer_store_b32(packed, rd, off[g] == kOutOfRange ? kOutOfRange : c / 2u, 0,
+                                            kStoreAux);
+      if (!(lane & 1) && c < ku) row_scale[(int64_t)r * (k / 16) + c / 16] = (uint8_t)S;
+    }
+  };
+
+  uint32_t va[NSEG][4], vb[NSEG][4];
+  uint32_t r = w0;
+  if (r < total) load_row(r, va);
+#pragma unroll 1
+  for (; r < total; r += 2 * nwaves) {
+    const uint32_t r1 = r + nwaves;
+    if (r1 < total) load_row(r1, vb);
+    do_row(r, va);
+    if (r1 >= total) break;
+    const uint32_t r2 = r1 + nwaves;
+    if (r2 < total) load_row(r2, va);
+    do_row(r1, vb);
+  }
+}
+
 // ------------------------------------------------------------- host side
 
 constexpr int64_t kMaxK = NVFP4G_MAX_K;
@@ -664,6 +756,26 @@ int launch_cast(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, co
   return hip_status();
 }
 
+// Fused rowwise amax + cast (K <= 8192): one wave per row at a time over a
+// grid of resident workgroups.
+constexpr int64_t kRowFusedMaxK = 8192;
+
+int launch_rowwise_fused(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, float* row_amax,
+                         uint8_t* row_data, uint8_t* row_scale, hipStream_t st) {
+  if (rows == 0) return NVFP4G_OK;
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((rows + 3) / 4, 2048));
+  if (k <= 2048)
+    hipLaunchKernelGGL(group_quantize_rowwise_kernel<4>, dim3(grid), dim3(kThreads), 0, st, x, k, R, row_amax,
+                       row_data, row_scale);
+  else if (k <= 4096)
+    hipLaunchKernelGGL(group_quantize_rowwise_kernel<8>, dim3(grid), dim3(kThreads), 0, st, x, k, R, row_amax,
+                       row_data, row_scale);
+  else
+    hipLaunchKernelGGL(group_quantize_rowwise_kernel<16>, dim3(grid), dim3(kThreads), 0, st, x, k, R, row_amax,
+                       row_data, row_scale);
+  return hip_status();
+}
+
 int graph_routing(const int32_t* d_offs, int32_t* d_status, int32_t E, int64_t m_capacity, Routing* R) {
   if (E < 1 || E > NVFP4G_MAX_EXPERTS_DEVICE) return NVFP4G_EINVAL;
   if (!d_offs || !d_status || m_capacity % kTileRows != 0) return NVFP4G_EINVAL;
@@ -735,6 +847,8 @@ int nvfp4_group_quantize(const uint16_t* x, int64_t sum_m, int64_t k, int32_t nu
   if ((rc = host_routing(h_splits, sum_m, num_experts, &R))) return rc;
   if ((rc = check_cast_outputs(row_amax, col_amax, row_data, row_scale, col_data, col_scale))) return rc;
   hipStream_t st = (hipStream_t)stream;
+  if (row_data && !col_data && k <= kRowFusedMaxK)
+    return launch_rowwise_fused(x, sum_m, k, R, row_amax, row_data, row_scale, st);
   if ((rc = launch_amax(x, sum_m, k, R, row_data ? row_amax : nullptr, col_data ? col_amax : nullptr, st)))
     return rc;
   return launch_cast(x, sum_m, k, R, row_amax, col_amax, row_data, row_scale, col_data, col_scale, st);
@@ -750,6 +864,8 @@ int nvfp4_group_quantize_graphsafe(const uint16_t* x, int64_t m_capacity, int64_
   if ((rc = graph_routing(d_offs, d_status, num_experts, m_capacity, &R))) return rc;
   if ((rc = check_cast_outputs(row_amax, col_amax, row_data, row_scale, col_data, col_scale))) return rc;
   hipStream_t st = (hipStream_t)stream;
+  if (row_data && !col_data && k <= kRowFusedMaxK)
+    return launch_rowwise_fused(x, m_capacity, k, R, row_amax, row_data, row_scale, st);
   if ((rc = launch_amax(x, m_capacity, k, R, row_data ? row_amax : nullptr, col_data ? col_amax : nullptr,
                         st)))
     return rc;

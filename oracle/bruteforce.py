@@ -10,8 +10,8 @@ fixed reading:
     m = 1/d (0 if d == 0, clamped to FLT_MAX);  code = E2M1(x*m)
 
 (per-token NVFP4 from "Implement per-token NVFP4 fprop recipe", Description;
-grouped amax and cast from "[Common] Single-launch grouped row-scaled NVFP4
-cast", Description).  Meant for tiny inputs: it is vectorised over elements
+grouped amax and cast from the TransformerEngine issue 3649 page
+(single-launch grouped row-scaled NVFP4 cast), Description).  Meant for tiny inputs: it is vectorised over elements
 but tries all 16 (or 127) candidates for each one.
 """
 from __future__ import annotations

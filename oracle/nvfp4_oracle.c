@@ -12,8 +12,8 @@
  * round-to-nearest-even, as written.
  *
  * Sources (the pages this follows; cited by page title and section):
- *  - "[Common] Single-launch grouped row-scaled NVFP4 cast" (TransformerEngine
- *    issue 3649), Description: a grouped amax over the packed (sum_M, K)
+ *  - the TransformerEngine issue 3649 page (single-launch grouped
+ *    row-scaled NVFP4 cast), Description: a grouped amax over the packed (sum_M, K)
  *    buffer yields a rowwise [sum_M] and a columnwise [num_tensors*K] amax,
  *    then a grouped cast consumes them; a graph-safe twin reads the routing
  *    from device offsets and is byte-identical.
@@ -24,8 +24,9 @@
  *  - "[PyTorch] Enable NVFP4 row-scaled (per-token) backward for
  *    GroupedLinear" (TransformerEngine PR 3324), Greptile Summary: the
  *    columnwise (transposed) operand carries a per-column amax.
- *  - "Make CustomRecipe usable for grouped GEMM ..." (TransformerEngine PR
- *    3824), Changes item 2: a 0-element split must not fail.
+ *  - the TransformerEngine PR 3824 page (CustomRecipe for grouped GEMM and
+ *    the MXFP4 reference quantizer), Changes item 2: a 0-element split must
+ *    not fail.
  *
  * The numerics (the pages print no formula; this is the project's fixed
  * reading, stated once here and in the design notes):
