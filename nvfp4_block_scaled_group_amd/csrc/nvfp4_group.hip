@@ -37,8 +37,11 @@
 #include <float.h>
 
 #include "../../include/nvfp4_group.h"
+#include "nvfp4_numerics.hpp"
 
 namespace {
+
+using namespace nvfp4g;
 
 constexpr int kThreads = 256;    // 4 wave64
 constexpr int kTileRows = 128;   // expert groups are multiples of 128 rows
@@ -98,155 +101,6 @@ __device__ __forceinline__ int find_expert(const Routing& R, int32_t row,
   return lo;
 }
 
-// ------------------------------------------------------------ bit helpers
-
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pkmax(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
-      __builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b)));
-}
-
-__device__ __forceinline__ uint32_t hmax(uint32_t a) {  // max of the two halves
-  return max(a & 0xFFFFu, a >> 16);
-}
-
-// DPP row_ror:8 inside a 16-lane row == lane ^ 8.
-__device__ __forceinline__ uint32_t swap8(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
-}
-// quad_perm [1,0,3,2] == lane ^ 1; quad_perm [2,3,0,1] == lane ^ 2;
-// row_half_mirror maps lane i of an 8-lane half row to 7 - i.
-__device__ __forceinline__ uint32_t dpp_x1(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t dpp_x2(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t dpp_hmirror(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
-}
-
-// gfx950 cross-row swaps: permlane32_swap(a, b) exchanges lanes 32..63 of a
-// with lanes 0..31 of b; permlane16_swap(a, b) exchanges the odd 16-lane rows
-// of a with the even rows of b.  The max of the two results is the max over
-// lane pairs l, l^32 (resp. l, l^16) of a in the lower half (even rows) and of
-// b in the upper half (odd rows).
-__device__ __forceinline__ uint32_t swap32_max(uint32_t a, uint32_t b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-  return pkmax(r[0], r[1]);
-}
-__device__ __forceinline__ uint32_t swap16_max(uint32_t a, uint32_t b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  return pkmax(r[0], r[1]);
-}
-
-// Reduce-scatter of 8 packed values over the 64 lanes of a wave: returns, in
-// every lane, the max over all lanes of value[lane >> 3].
-__device__ __forceinline__ uint32_t wave_reduce_scatter8(const uint32_t (&v)[8], int lane) {
-  uint32_t n[4], m[2];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) n[p] = swap32_max(v[p], v[p + 4]);  // value p + 4*bit5
-#pragma unroll
-  for (int q = 0; q < 2; ++q) m[q] = swap16_max(n[q], n[q + 2]);  // + 2*bit4
-  const bool b3 = (lane >> 3) & 1;                                  // + bit3
-  uint32_t r = pkmax(b3 ? m[1] : m[0], swap8(b3 ? m[0] : m[1]));
-  r = pkmax(r, dpp_x1(r));
-  r = pkmax(r, dpp_x2(r));
-  return pkmax(r, dpp_hmirror(r));
-}
-
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// ---------------------------------------------------------------- numerics
-
-// E4M3FN code of t >= 0 (finite or +inf): nearest, ties to even, saturating
-// at 448 (0x7E).  Normal range: round the fp32 mantissa to 3 bits and
-// re-bias the exponent (7 - 127); subnormal range (t < 2^-6): the nearest
-// multiple of 2^-9, found by adding 2^14 (whose fp32 spacing is 2^-9).
-__device__ __forceinline__ uint32_t e4m3_code(float t) {
-  if (t >= 448.0f) return 0x7Eu;
-  const uint32_t tb = __float_as_uint(t);
-  if (tb >= 0x3C800000u) {  // t >= 2^-6
-    const uint32_t r = (tb + 0x7FFFFu + ((tb >> 20) & 1u)) >> 20;
-    return r - (120u << 3);
-  }
-  return __float_as_uint(t + 16384.0f) - 0x46800000u;
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = c >> 3, f = c & 7u;
-  return e ? __uint_as_float(((e + 120u) << 23) | (f << 20))
-           : (float)f * 0.001953125f;  // f * 2^-9, exact
-}
-
-// Block step: E4M3 scale code of a block with amax b on a line with scale s,
-// and the element multiplier m = 1 / (value(S) * s).
-__device__ __forceinline__ uint32_t block_scale(float b, float s, float* m) {
-  const float t = (s == 0.0f) ? 0.0f : (b / 6.0f) / s;
-  const uint32_t S = e4m3_code(t);
-  const float d = e4m3_value(S) * s;
-  *m = (d == 0.0f) ? 0.0f : fminf(1.0f / d, FLT_MAX);
-  return S;
-}
-
-// Same step with fewer operations, for line scales s >= 2^-112 (line amax of
-// about 2^-100.6 or more), given ys = 1/s (correctly rounded, once per line):
-//   u = b/6 as q0 = b*RN(1/6) plus one fused residual correction,
-//   t = u/s as t0 = u*ys plus one fused residual correction,
-//   m = 1/d as the hardware reciprocal plus one Newton step.
-// Over every pair of bf16 values b <= A with A >= 2^-102 this gives the same
-// E4M3 code, and (for A >= 2^-105) the same m bits, as the correctly rounded
-// divisions above; smaller lines take the exact path.
-constexpr float kFastMinLineScale = 0x1p-112f;
-
-__device__ __forceinline__ uint32_t block_scale_fast(float b, float s, float ys, float* m) {
-  const float r6 = 0x1.555556p-3f;  // RN(1/6)
-  const float q0 = b * r6;
-  const float u = __builtin_fmaf(__builtin_fmaf(-6.0f, q0, b), r6, q0);
-  const float t0 = u * ys;
-  const float t = __builtin_fmaf(__builtin_fmaf(-s, t0, u), ys, t0);
-  const uint32_t S = e4m3_code(t);
-  const float d = e4m3_value(S) * s;
-  const float y0 = __builtin_amdgcn_rcpf(d);
-  const float y1 = __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
-  *m = (d == 0.0f) ? 0.0f : fminf(y1, FLT_MAX);
-  return S;
-}
-
-__device__ __forceinline__ uint32_t block_step(float b, float s, float ys, float* m) {
-  if (s >= kFastMinLineScale) return block_scale_fast(b, s, ys, m);
-  return block_scale(b, s, m);
-}
-
-// Hardware FP4 conversion (gfx950): two fp32 values -> one E2M1x2 byte
-// (first value in the low nibble) placed at byte SEL of `old`.  With scale
-// 1.0 it rounds to nearest (ties to the even code), saturates at +-6 and
-// keeps the sign of zero: it equals e2m1_code below on every non-NaN fp32
-// input.
-#define FP4X2(old, a, b, SEL) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (SEL))
-
-// 4-bit E2M1 code of v: sign bit of v, magnitude nearest on
-// {0, .5, 1, 1.5, 2, 3, 4, 6} with ties to the even code, saturating.
-// |v| >= 1: round the fp32 mantissa to 1 bit; the code is then the fp32
-// exponent/mantissa re-biased (code 2 = 1.0).  |v| < 1: the code is the
-// nearest integer (ties even) to 2|v|.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const uint32_t vb = __float_as_uint(v);
-  const uint32_t sign = (vb >> 28) & 8u;
-  const uint32_t a = vb & 0x7FFFFFFFu;
-  uint32_t hi = (a + 0x1FFFFFu + ((a >> 22) & 1u) - 0x3F000000u) >> 22;
-  hi = min(hi, 7u);
-  const uint32_t lo = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
-  return sign | (a >= 0x3F800000u ? hi : lo);
-}
-
-// Two packed bf16 (element 2j low, 2j+1 high) -> one FP4x2 byte.
-__device__ __forceinline__ uint32_t enc_pair(uint32_t w, float m) {
-  return e2m1_code(bf16lo(w) * m) | (e2m1_code(bf16hi(w) * m) << 4);
-}
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 
@@ -281,30 +135,23 @@ __global__ __launch_bounds__(kThreads) void amax_init_kernel(
   }
 }
 
-// Work decomposition shared by both kernels.  The (sum_M x K) buffer is cut
-// into strips of kStrip consecutive 128-row sub-tiles by chunks of 256
-// columns; a workgroup walks one strip top to bottom, so the transposed
-// lines it writes are contiguous over its whole strip, and the column amax
-// of a strip needs one flush per expert it touches.  Workgroups are
-// dispatched round-robin over the 8 XCDs (each with its own L2), so the
-// linear block id is remapped to give each XCD a contiguous range of strips:
-// vertically adjacent strips, which write the two halves of shared output
-// lines, then go through the same L2.
-#ifndef NVFP4G_STRIP
-#define NVFP4G_STRIP 1
-#endif
-constexpr int kStrip = NVFP4G_STRIP;
+// Tile order of the cast kernel.  Work-groups are dispatched round-robin
+// over the 8 XCDs, each with its own L2; the linear block id is remapped so
+// that each XCD gets a contiguous run of logical tiles, ordered row tile
+// first within a 256-column chunk.  Vertically adjacent tiles, which write
+// the two 64-byte halves of each 128-byte line of the transposed output, then
+// go through the same L2 at about the same time.
 constexpr int kNumXcd = 8;
 
 struct TileCoord {
-  uint32_t strip, chunk;
+  uint32_t row_tile, chunk;
 };
 
-__device__ __forceinline__ TileCoord tile_coord(uint32_t nstrips) {
+__device__ __forceinline__ TileCoord tile_coord(uint32_t nrow_tiles) {
   const uint32_t nb = gridDim.x, L = blockIdx.x;
   const uint32_t xcd = L % kNumXcd, q = nb / kNumXcd, r = nb % kNumXcd;
   const uint32_t lt = xcd * q + min(xcd, r) + L / kNumXcd;  // a permutation of 0..nb-1
-  return TileCoord{uni(lt % nstrips), uni(lt / nstrips)};
+  return TileCoord{uni(lt % nrow_tiles), uni(lt / nrow_tiles)};
 }
 
 // Loads the lane's 16 rows x 8 columns (16 x 16 bytes) of a 128 x 256 tile
@@ -443,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void group_amax_kernel(
   if (col_amax && key_e >= 0) flush_cols();
 }
 
-// Grouped cast over one strip x 256 columns; rowwise and/or columnwise.
+// Grouped cast of one 128 x 256 tile; rowwise and/or columnwise.
 //
 // Addressing: every tensor is reached through a raw buffer descriptor whose
 // base is the tile's first element, a per-lane 32-bit offset and a scalar
@@ -452,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void group_amax_kernel(
 // past the descriptor's range: their loads return 0 and their stores are
 // dropped by the hardware range check.
 __global__ __launch_bounds__(kThreads) void group_cast_kernel(
-    const uint16_t* __restrict__ x, int64_t k, Routing R, uint32_t nstrips,
+    const uint16_t* __restrict__ x, int64_t k, Routing R, uint32_t nrow_tiles,
     const float* __restrict__ row_amax, const float* __restrict__ col_amax,
     uint8_t* __restrict__ row_data, uint8_t* __restrict__ row_scale,
     uint8_t* __restrict__ col_data, uint8_t* __restrict__ col_scale) {
@@ -462,9 +309,9 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
   __shared__ uint32_t l_cs[kTileCols][2];               // column scales, 8 per column
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
-  const TileCoord tc = tile_coord(nstrips);
-  const int32_t strip_row0 = (int32_t)tc.strip * kStrip * kTileRows;
-  if (strip_row0 >= total) return;
+  const TileCoord tc = tile_coord(nrow_tiles);
+  const int32_t row0 = (int32_t)tc.row_tile * kTileRows;
+  if (row0 >= total) return;
   const int64_t col_base = (int64_t)tc.chunk * kTileCols;
   const uint32_t ncols = (uint32_t)min<int64_t>(k - col_base, kTileCols);
   const uint32_t ku = (uint32_t)k;
@@ -475,28 +322,21 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
   const uint32_t lcol = wave * 64 + cg * 8;  // lane's first column within the tile
   const bool active = lcol < ncols;
   const uint32_t vo_x = active ? (16u * rb * ku + lcol) * 2u : kOutOfRange;
-  int e_cur = -1;
-
-#pragma unroll 1
-  for (int h = 0; h < kStrip; ++h) {
-    const int32_t row0 = strip_row0 + h * kTileRows;
-    if (row0 >= total) break;
+  {
     int32_t rbeg, rend;
     const int e = find_expert(R, row0, &rbeg, &rend);
     const uint32_t me = (uint32_t)(rend - rbeg);
 
     uint32_t v[16][4];
     load_tile(x + (int64_t)row0 * k + col_base, ku, vo_x, v);
-    if (h) __syncthreads();  // the previous sub-tile is done with the LDS tables
     if (row_data && tid < kTileRows) {
       const float s = row_amax[row0 + tid] / 2688.0f;
       l_row[tid] = make_float2(s, 1.0f / s);
     }
-    if (col_data && e != e_cur) {
+    if (col_data) {
       const float s = (uint32_t)tid < ncols ? col_amax[(int64_t)e * k + col_base + tid] / 2688.0f : 0.0f;
       l_col[tid] = make_float2(s, 1.0f / s);
     }
-    e_cur = e;
     __syncthreads();
 
     if (row_data) {
@@ -717,11 +557,6 @@ int check_cast_outputs(const float* row_amax, const float* col_amax, const uint8
   return NVFP4G_OK;
 }
 
-// Number of strips (kStrip x 128 rows) covering `rows` rows, and the 1-D
-// grid of strips x 256-column chunks.
-uint32_t num_strips(int64_t rows) {
-  return (uint32_t)((rows + kStrip * kTileRows - 1) / (kStrip * kTileRows));
-}
 // Persistent amax grid: enough resident workgroups to cover the device
 // (at most the number of 64 x 512 tiles of the buffers).
 #ifndef NVFP4G_AMAX_WGS
@@ -731,8 +566,10 @@ unsigned amax_grid(int64_t rows, int64_t k) {
   const int64_t tiles = (rows / kAmaxRows) * ((k + kAmaxCols - 1) / kAmaxCols);
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(tiles, NVFP4G_AMAX_WGS));
 }
+// 1-D grid of 128-row tiles x 256-column chunks for the cast kernel.
+uint32_t num_row_tiles(int64_t rows) { return (uint32_t)((rows + kTileRows - 1) / kTileRows); }
 dim3 tile_grid(int64_t rows, int64_t k) {
-  return dim3(num_strips(rows) * (unsigned)((k + kTileCols - 1) / kTileCols));
+  return dim3(num_row_tiles(rows) * (unsigned)((k + kTileCols - 1) / kTileCols));
 }
 
 int launch_amax(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, float* row_amax,
@@ -751,7 +588,7 @@ int launch_cast(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, co
                 const float* col_amax, uint8_t* row_data, uint8_t* row_scale, uint8_t* col_data,
                 uint8_t* col_scale, hipStream_t st) {
   if ((!row_data && !col_data) || rows == 0) return NVFP4G_OK;
-  hipLaunchKernelGGL(group_cast_kernel, tile_grid(rows, k), dim3(kThreads), 0, st, x, k, R, num_strips(rows), row_amax,
+  hipLaunchKernelGGL(group_cast_kernel, tile_grid(rows, k), dim3(kThreads), 0, st, x, k, R, num_row_tiles(rows), row_amax,
                      col_amax, row_data, row_scale, col_data, col_scale);
   return hip_status();
 }

@@ -1,0 +1,110 @@
+// nvfp4_selftest.hip -- test-only GPU library that runs the device numerics
+// of libnvfp4g.so (csrc/nvfp4_numerics.hpp) exhaustively or on given samples,
+// for tests/test_gpu_numerics.py.  Not part of the product library.
+//
+//  * the hardware FP4 convert (FP4X2, scale 1.0) against the software E2M1
+//    rule (e2m1_code) on every non-NaN fp32 pattern, both nibble positions;
+//  * the kernels' block step (fast path for line scales >= 2^-112, IEEE
+//    divisions below) against the IEEE-division block step on every pair of
+//    bf16 values b <= A (b = block amax, A = line amax);
+//  * sample outputs (block step, FP4 codes) that the tests compare with the
+//    CPU oracle.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../nvfp4_block_scaled_group_amd/csrc/nvfp4_numerics.hpp"
+
+using namespace nvfp4g;
+
+namespace {
+
+__global__ void fp4_exhaustive_kernel(unsigned long long* counts, uint32_t base) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  unsigned long long n = 0, bad_lo = 0, bad_hi = 0;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 31); i += stride) {
+    const float v = __uint_as_float(base + (uint32_t)i);
+    if (v != v) continue;
+    const uint32_t sw = e2m1_code(v);
+    const uint32_t lo = FP4X2(0u, v, 0.0f, 0) & 0xFFu;
+    const uint32_t hi = FP4X2(0u, 0.0f, v, 0) & 0xFFu;
+    n++;
+    bad_lo += lo != sw;            // v in the low nibble, +0 (code 0) in the high one
+    bad_hi += hi != (sw << 4);     // v in the high nibble
+  }
+  atomicAdd(&counts[0], n);
+  atomicAdd(&counts[1], bad_lo);
+  atomicAdd(&counts[2], bad_hi);
+}
+
+// one workgroup per line amax A (bf16 pattern 1..0x7F7F), b over 0..A
+__global__ void block_step_exhaustive_kernel(unsigned long long* counts) {
+  const uint32_t A16 = 1u + blockIdx.x;
+  const float A = __uint_as_float(A16 << 16);
+  const float s = A / 2688.0f, ys = 1.0f / s;
+  unsigned long long n = 0, badS = 0, badm = 0;
+  for (uint32_t b16 = threadIdx.x; b16 <= A16; b16 += blockDim.x) {
+    const float b = __uint_as_float(b16 << 16);
+    float m1, m2;
+    const uint32_t S1 = block_scale(b, s, &m1);
+    const uint32_t S2 = block_step(b, s, ys, &m2);
+    n++;
+    badS += S1 != S2;
+    badm += __float_as_uint(m1) != __float_as_uint(m2);
+  }
+  atomicAdd(&counts[0], n);
+  atomicAdd(&counts[1], badS);
+  atomicAdd(&counts[2], badm);
+}
+
+__global__ void block_step_sample_kernel(const uint16_t* b16, const uint16_t* A16, int64_t n, uint8_t* S,
+                                         float* m) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float A = __uint_as_float((uint32_t)A16[i] << 16);
+  const float s = A / 2688.0f, ys = 1.0f / s;
+  float mm;
+  S[i] = (uint8_t)block_step(__uint_as_float((uint32_t)b16[i] << 16), s, ys, &mm);
+  m[i] = mm;
+}
+
+__global__ void fp4_codes_kernel(const float* v, int64_t n, uint8_t* codes) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  codes[i] = (uint8_t)(FP4X2(0u, v[i], 0.0f, 0) & 0xFu);
+}
+
+int status() { return hipGetLastError() == hipSuccess ? 0 : -4; }
+
+}  // namespace
+
+extern "C" {
+
+// counts (device, 3 x u64, zeroed by the caller): patterns, low-nibble and
+// high-nibble mismatches.
+int selftest_fp4_exhaustive(unsigned long long* counts) {
+  hipLaunchKernelGGL(fp4_exhaustive_kernel, dim3(4096), dim3(256), 0, 0, counts, 0u);
+  hipLaunchKernelGGL(fp4_exhaustive_kernel, dim3(4096), dim3(256), 0, 0, counts, 0x80000000u);
+  return status();
+}
+
+// counts (device, 3 x u64, zeroed by the caller): pairs, scale-code and
+// multiplier-bit mismatches.
+int selftest_block_step_exhaustive(unsigned long long* counts) {
+  hipLaunchKernelGGL(block_step_exhaustive_kernel, dim3(0x7F7F), dim3(256), 0, 0, counts);
+  return status();
+}
+
+int selftest_block_step_sample(const uint16_t* b16, const uint16_t* A16, int64_t n, uint8_t* S, float* m) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(block_step_sample_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, 0, b16, A16, n,
+                     S, m);
+  return status();
+}
+
+int selftest_fp4_codes(const float* v, int64_t n, uint8_t* codes) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(fp4_codes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, 0, v, n, codes);
+  return status();
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+"""Exhaustive and sampled checks of the device numerics on the GPU.
+
+The kernels quantise with gfx950's hardware FP4 convert and with a block
+step whose fast path replaces three correctly rounded divisions by fused
+corrections.  These tests prove both equal to their plain definitions on
+every input they can receive, and pin GPU outputs to the CPU oracle:
+
+* hardware FP4 convert == the software E2M1 rule, on all 2^32 - 2^24 non-NaN
+  fp32 patterns, in both nibble positions;
+* the kernels' block step == the IEEE-division block step, on every pair of
+  bf16 values b <= A (532,701,119 pairs: every block amax / line amax pair a
+  bf16 input can produce);
+* GPU block steps and FP4 codes == the oracle on large structured samples.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+
+from gpu_helpers import log
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "hip", "libnvfp4g_selftest.so")
+P = ctypes.c_void_p
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is not built; run tests/hip/build_selftest.py")
+    L = ctypes.CDLL(LIB)
+    L.selftest_fp4_exhaustive.argtypes = [P]
+    L.selftest_block_step_exhaustive.argtypes = [P]
+    L.selftest_block_step_sample.argtypes = [P, P, ctypes.c_int64, P, P]
+    L.selftest_fp4_codes.argtypes = [P, ctypes.c_int64, P]
+    return L
+
+
+def ptr(t):
+    return P(t.data_ptr())
+
+
+def test_fp4_convert_equals_software_rule_on_every_fp32(lib):
+    log("fp4 convert, all fp32 patterns")
+    c = torch.zeros(3, dtype=torch.int64, device="cuda:0")
+    assert lib.selftest_fp4_exhaustive(ptr(c)) == 0
+    n, bad_lo, bad_hi = c.cpu().tolist()
+    assert n == (1 << 32) - 2 * ((1 << 23) - 1)  # all but the NaN patterns
+    assert bad_lo == 0 and bad_hi == 0
+
+
+def test_block_step_equals_ieee_divisions_on_every_bf16_pair(lib):
+    log("block step, all bf16 pairs b <= A")
+    c = torch.zeros(3, dtype=torch.int64, device="cuda:0")
+    assert lib.selftest_block_step_exhaustive(ptr(c)) == 0
+    n, bad_s, bad_m = c.cpu().tolist()
+    amax16 = np.arange(1, 0x7F80, dtype=np.int64)
+    assert n == int((amax16 + 1).sum())
+    assert bad_s == 0 and bad_m == 0
+
+
+def _pairs(rng, n):
+    """bf16 patterns b <= A: uniform over the finite range, plus line amax near
+    the fast path's threshold, tiny and subnormal lines, b = A and b = 0."""
+    A = rng.integers(1, 0x7F80, n).astype(np.uint16)
+    A[: n // 8] = rng.integers(0x0A00, 0x0E00, n // 8)      # A around 2^-107 .. 2^-99
+    A[n // 8: n // 4] = rng.integers(1, 0x0100, n // 8)      # bf16 subnormal / tiny lines
+    b = (rng.random(n) * (A.astype(np.float64) + 1)).astype(np.uint16)
+    b = np.minimum(b, A)
+    b[: 64] = A[: 64]
+    b[64: 128] = 0
+    return b, A
+
+
+def test_block_step_sample_matches_oracle(lib):
+    rng = np.random.default_rng(3)
+    b, A = _pairs(rng, 1 << 20)
+    log("block step sample vs oracle")
+    db = torch.from_numpy(b.view(np.int16)).cuda()
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    S = torch.empty(b.size, dtype=torch.uint8, device="cuda:0")
+    m = torch.empty(b.size, dtype=torch.float32, device="cuda:0")
+    assert lib.selftest_block_step_sample(ptr(db), ptr(dA), b.size, ptr(S), ptr(m)) == 0
+    torch.cuda.synchronize()
+    bf = (b.astype(np.uint32) << 16).view(np.float32)
+    Af = (A.astype(np.uint32) << 16).view(np.float32)
+    s = (Af / np.float32(2688.0)).astype(np.float32)            # IEEE fp32 division
+    rS, rm = O.block_scale(bf, s)
+    assert (S.cpu().numpy() == rS).all()
+    assert (m.cpu().numpy().view(np.uint32) == rm.view(np.uint32)).all()
+
+
+def test_fp4_codes_match_oracle(lib):
+    # every 37th fp32 pattern up to 8.0, the E2M1 midpoints and their
+    # neighbours, denormals, large values, infinities and both zeros, with
+    # both signs
+    bits = np.arange(0, 0x41000000, 37, dtype=np.uint32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    extra = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf)),
+                            np.array([0.0, 1e-45, 1e-40, 6.0, 6.5, 1e30, np.inf], np.float32)])
+    v = np.concatenate([bits.view(np.float32), extra])
+    v = np.concatenate([v, -v])
+    log(f"fp4 codes vs oracle, {v.size} values")
+    dv = torch.from_numpy(v).cuda()
+    codes = torch.empty(v.size, dtype=torch.uint8, device="cuda:0")
+    assert lib.selftest_fp4_codes(ptr(dv), v.size, ptr(codes)) == 0
+    torch.cuda.synchronize()
+    assert (codes.cpu().numpy() == O.e2m1_encode(v)).all()
