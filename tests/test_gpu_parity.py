@@ -265,3 +265,45 @@ def test_graph_capture_replays_under_new_routing():
             assert_equal_outputs(host, oracle_ref(synth.Workload("r", xb, np.array(splits, np.int64))))
     assert int(d_status.item()) == 0
     assert_guards(out)
+
+
+# ------------------------------------------------------- more shapes / entries
+
+@pytest.mark.parametrize("k", [16, 528, 2048, 2064, 4096, 8192, 8208])
+def test_rowwise_quantize_fused_and_fallback(k):
+    # K <= 8192 runs the one-pass rowwise kernel (4, 8 or 16 column segments
+    # per lane); K = 8208 falls back to amax + cast.  Both equal the oracle.
+    w = synth.random_case(50 + k, [256, 0, 128], k, "outliers")
+    check_small(w, True, False, entry="quantize")
+
+
+def test_rowwise_graphsafe_quantize_equals_host_split():
+    w = synth.random_case(61, [128, 384, 0, 256], 1040, "rowscale")
+    splits = list(map(int, w.splits))
+    log("graph-safe rowwise quantize")
+    x = to_device(w.x)
+    host = to_numpy(run_host_split(x, splits, True, False, entry="quantize"))
+    out = alloc(w.sum_m, w.k, len(splits), True, False)
+    d_offs = torch.tensor(B.offsets_from_splits(splits), dtype=torch.int32, device="cuda:0")
+    d_status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    B.nvfp4_group_quantize_graphsafe(x, len(splits), d_offs, d_status, **tensors(out))
+    torch.cuda.synchronize()
+    assert int(d_status.item()) == 0
+    assert_guards(out)
+    assert_equal_outputs(to_numpy(out), host)
+    assert_equal_outputs(host, oracle_ref(w, True, False), ["row_amax", "row_data", "row_scale"])
+
+
+def test_many_experts_and_one_expert():
+    # 96 experts of mixed sizes (many empty), and a single expert
+    rng = np.random.default_rng(62)
+    splits = (rng.integers(0, 3, 96) * 128).tolist()
+    splits[5] = 0
+    check_small(synth.random_case(63, splits, 80, "normal"))
+    check_small(synth.random_case(64, [1024], 272, "rowscale"))
+
+
+def test_max_host_experts_mostly_empty():
+    splits = [0] * 512
+    splits[0], splits[200], splits[511] = 128, 256, 128
+    check_small(synth.random_case(65, splits, 32, "normal"))
