@@ -147,6 +147,35 @@ int nvfp4_group_quantize_graphsafe(const uint16_t* x, int64_t m_capacity,
                                    uint8_t* col_scale, int32_t* d_status,
                                    void* stream);
 
+/* Dequantisation of row-scaled NVFP4 ("Implement per-token NVFP4 fprop
+ * recipe", TransformerEngine PR 2931, Important Files Changed: the dequant
+ * looks the amax up by the element's row).  Element i of a line with amax A
+ * and block scale S:  out = (value(code) * value(S)) * (A / 2688)  (fp32).
+ *
+ * Rowwise: row_data [rows, k/2], row_scale [rows, k/16], row_amax [rows]
+ * -> out fp32 [rows, k].  Rows are independent (pass the routed row count). */
+int nvfp4_group_dequant_rowwise(const uint8_t* row_data, const uint8_t* row_scale,
+                                const float* row_amax, int64_t rows, int64_t k,
+                                float* out, void* stream);
+
+/* Columnwise: the transposed output of nvfp4_group_cast (per expert [k, M_e]
+ * lines with amax col_amax[e*k + c]) -> out fp32 in the same transposed
+ * layout: expert e's block of k lines of M_e values at element offset k*r_e. */
+int nvfp4_group_dequant_columnwise(const uint8_t* col_data, const uint8_t* col_scale,
+                                   const float* col_amax, int64_t sum_m, int64_t k,
+                                   int32_t num_experts, const int64_t* h_splits,
+                                   float* out, void* stream);
+
+/* Graph-safe columnwise dequant: routing from d_offs as in
+ * nvfp4_group_cast_graphsafe; elements beyond k*offs[E-1] are not written. */
+int nvfp4_group_dequant_columnwise_graphsafe(const uint8_t* col_data,
+                                             const uint8_t* col_scale,
+                                             const float* col_amax,
+                                             int64_t m_capacity, int64_t k,
+                                             int32_t num_experts,
+                                             const int32_t* d_offs, float* out,
+                                             int32_t* d_status, void* stream);
+
 /* Static description of a status code. */
 const char* nvfp4_group_strerror(int status);
 

@@ -33,6 +33,8 @@ MAX_EXPERTS_DEVICE = 4096
 EXPORTS = (
     "nvfp4_group_amax", "nvfp4_group_cast", "nvfp4_group_amax_graphsafe",
     "nvfp4_group_cast_graphsafe", "nvfp4_group_quantize", "nvfp4_group_quantize_graphsafe",
+    "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
+    "nvfp4_group_dequant_columnwise_graphsafe",
     "nvfp4_group_strerror",
 )
 
@@ -62,6 +64,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.nvfp4_group_cast_graphsafe.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     L.nvfp4_group_quantize.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P]
     L.nvfp4_group_quantize_graphsafe.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    L.nvfp4_group_dequant_rowwise.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
+    L.nvfp4_group_dequant_columnwise.argtypes = [_P, _P, _P, _I64, _I64, _I32, _P, _P, _P]
+    L.nvfp4_group_dequant_columnwise_graphsafe.argtypes = [_P, _P, _P, _I64, _I64, _I32, _P, _P, _P, _P]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = ctypes.c_int
     L.nvfp4_group_strerror.argtypes = [ctypes.c_int]
@@ -157,6 +162,29 @@ def nvfp4_group_quantize_graphsafe(x, num_experts, d_offs, d_status, row_amax=No
     _check("nvfp4_group_quantize_graphsafe", load_library().nvfp4_group_quantize_graphsafe(
         xp, m, k, int(num_experts), _ptr(d_offs), _ptr(row_amax), _ptr(col_amax), _ptr(row_data),
         _ptr(row_scale), _ptr(col_data), _ptr(col_scale), _ptr(d_status), _stream(stream)))
+
+
+def nvfp4_group_dequant_rowwise(row_data, row_scale, row_amax, out, stream=None):
+    """row_data [rows, k/2] u8, row_scale [rows, k/16] u8, row_amax [rows] f32 -> out [rows, k] f32."""
+    rows, half_k = row_data.shape
+    _check("nvfp4_group_dequant_rowwise", load_library().nvfp4_group_dequant_rowwise(
+        _ptr(row_data), _ptr(row_scale), _ptr(row_amax), rows, 2 * half_k, _ptr(out), _stream(stream)))
+
+
+def nvfp4_group_dequant_columnwise(col_data, col_scale, col_amax, h_splits, k, out, stream=None):
+    """Transposed output (per expert [k, M_e] lines) -> out f32 in the same layout (k * sum_m values)."""
+    sp, e = _splits(h_splits)
+    sum_m = sum(int(v) for v in h_splits)
+    _check("nvfp4_group_dequant_columnwise", load_library().nvfp4_group_dequant_columnwise(
+        _ptr(col_data), _ptr(col_scale), _ptr(col_amax), sum_m, int(k), e, sp, _ptr(out), _stream(stream)))
+
+
+def nvfp4_group_dequant_columnwise_graphsafe(col_data, col_scale, col_amax, m_capacity, k, num_experts, d_offs,
+                                             out, d_status, stream=None):
+    _check("nvfp4_group_dequant_columnwise_graphsafe",
+           load_library().nvfp4_group_dequant_columnwise_graphsafe(
+               _ptr(col_data), _ptr(col_scale), _ptr(col_amax), int(m_capacity), int(k), int(num_experts),
+               _ptr(d_offs), _ptr(out), _ptr(d_status), _stream(stream)))
 
 
 # ---------------------------------------------------------------- helpers

@@ -1,0 +1,151 @@
+// nvfp4_common.hpp -- routing, buffer addressing and host-side argument
+// checks shared by the HIP sources of libnvfp4g.so.
+//
+// Routing: expert e owns rows [end(e-1), end(e)) of the packed buffer, with
+// end() the inclusive row ends, taken from the kernel arguments for host
+// splits or from device memory for the graph-safe calls (TransformerEngine
+// issue 3649 page, Description: the graph-safe twins read the routing from
+// device offsets and share the device body).  Every expert's row count is a
+// multiple of 128 (the token dispatcher pads groups to 128 rows, torchtitan
+// PR 14 page, Design notes).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4_group.h"
+
+namespace nvfp4g {
+
+constexpr int kThreads = 256;    // 4 wave64
+constexpr int kTileRows = 128;   // expert groups are multiples of 128 rows
+constexpr int kTileCols = 256;   // 4 waves x 64 columns
+
+// ------------------------------------------------------------------ routing
+
+struct Routing {
+  const int32_t* d_offs;  // device inclusive row ends (graph-safe) or null
+  int32_t* d_status;      // graph-safe status word
+  int32_t num_experts;
+  int32_t m_capacity;     // rows in the buffers
+  int32_t h_offs[NVFP4G_MAX_EXPERTS_HOST];  // host-split inclusive row ends
+};
+
+// Values that are uniform over a workgroup (routing, tile coordinates) are
+// passed through readfirstlane so the compiler keeps them, and the buffer
+// descriptors built from them, in scalar registers.
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+
+// Inclusive row end of expert e, for an e that is the same in every lane.
+__device__ __forceinline__ int32_t route_end(const Routing& R, int e) {
+  return uni(R.d_offs ? R.d_offs[e] : R.h_offs[e]);
+}
+// The same for an e that may differ between lanes.
+__device__ __forceinline__ int32_t route_end_lane(const Routing& R, int e) {
+  return R.d_offs ? R.d_offs[e] : R.h_offs[e];
+}
+
+// Device routing check (graph-safe calls only): every wave checks all
+// offsets; on failure the status bits are ORed in and the caller returns.
+__device__ bool routing_ok(const Routing& R) {
+  if (!R.d_offs) return true;
+  const int lane = threadIdx.x & 63;
+  uint32_t bad = 0;
+  for (int e = lane; e < R.num_experts; e += 64) {
+    const int32_t hi = R.d_offs[e];
+    const int32_t lo = e ? R.d_offs[e - 1] : 0;
+    if (hi < lo) bad |= NVFP4G_DEV_NONMONO;
+    if (hi & (kTileRows - 1)) bad |= NVFP4G_DEV_UNALIGNED;
+    if (hi > R.m_capacity) bad |= NVFP4G_DEV_OVERFLOW;
+  }
+  uint32_t all = 0;
+  if (__ballot(bad & NVFP4G_DEV_UNALIGNED)) all |= NVFP4G_DEV_UNALIGNED;
+  if (__ballot(bad & NVFP4G_DEV_NONMONO)) all |= NVFP4G_DEV_NONMONO;
+  if (__ballot(bad & NVFP4G_DEV_OVERFLOW)) all |= NVFP4G_DEV_OVERFLOW;
+  if (all && lane == 0 && R.d_status) atomicOr(R.d_status, (int32_t)all);
+  return all == 0;
+}
+
+// Expert owning row `row` (< total): first e with end(e) > row.
+__device__ __forceinline__ int find_expert(const Routing& R, int32_t row,
+                                           int32_t* begin, int32_t* end) {
+  int lo = 0, hi = R.num_experts - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (route_end(R, mid) > row) hi = mid; else lo = mid + 1;
+  }
+  *end = route_end(R, lo);
+  *begin = lo ? route_end(R, lo - 1) : 0;
+  return lo;
+}
+
+// ------------------------------------------------------------ addressing
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor (gfx9 layout: 32-bit data format word) over `base`.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+// Offset of a lane that must not touch memory: beyond the descriptor range.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache policy bits: streaming (non-temporal) loads of x; plain stores.
+constexpr int kLoadStream = 2;
+#ifndef NVFP4G_STORE_AUX
+#define NVFP4G_STORE_AUX 0
+#endif
+constexpr int kStoreAux = NVFP4G_STORE_AUX;
+
+// ------------------------------------------------------------- host side
+
+constexpr int64_t kMaxK = NVFP4G_MAX_K;
+constexpr int64_t kMaxRows = NVFP4G_MAX_ROWS;
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline int hip_status() {
+  return hipGetLastError() == hipSuccess ? NVFP4G_OK : NVFP4G_EHIP;
+}
+
+// Common static checks; fills R (all but the offsets).
+inline int check_common(const void* x, int64_t rows, int64_t k, int32_t E, Routing* R) {
+  // size limits keep every per-lane and per-row buffer offset below 2^31
+  if (k <= 0 || k % 16 != 0 || k > kMaxK) return NVFP4G_EINVAL;
+  if (rows < 0 || rows > kMaxRows) return NVFP4G_EINVAL;
+  if (rows > 0 && x == nullptr) return NVFP4G_EINVAL;
+  if (!aligned(x, 16)) return NVFP4G_EALIGN;
+  R->num_experts = E;
+  R->m_capacity = (int32_t)rows;
+  R->d_offs = nullptr;
+  R->d_status = nullptr;
+  return NVFP4G_OK;
+}
+
+inline int host_routing(const int64_t* h_splits, int64_t sum_m, int32_t E, Routing* R) {
+  if (E < 1 || E > NVFP4G_MAX_EXPERTS_HOST) return NVFP4G_EINVAL;
+  if (!h_splits) return NVFP4G_EINVAL;
+  int64_t acc = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    const int64_t m = h_splits[e];
+    if (m < 0 || m % kTileRows != 0) return NVFP4G_ESPLITS;
+    acc += m;
+    if (acc > sum_m) return NVFP4G_ESPLITS;
+    R->h_offs[e] = (int32_t)acc;
+  }
+  return acc == sum_m ? NVFP4G_OK : NVFP4G_ESPLITS;
+}
+
+inline int graph_routing(const int32_t* d_offs, int32_t* d_status, int32_t E, int64_t m_capacity, Routing* R) {
+  if (E < 1 || E > NVFP4G_MAX_EXPERTS_DEVICE) return NVFP4G_EINVAL;
+  if (!d_offs || !d_status || m_capacity % kTileRows != 0) return NVFP4G_EINVAL;
+  if (!aligned(d_offs, 4) || !aligned(d_status, 4)) return NVFP4G_EALIGN;
+  R->d_offs = d_offs;
+  R->d_status = d_status;
+  return NVFP4G_OK;
+}
+
+}  // namespace nvfp4g

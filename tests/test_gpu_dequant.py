@@ -1,0 +1,97 @@
+"""GPU dequantisation of row-scaled NVFP4 against the oracle's decode.
+
+The kernel and the oracle use the same op order, x^ = (value(code) *
+value(S)) * (A / 2688), so the fp32 results are compared bit for bit (a
+stricter form of the max-abs-error <= 1e-6 cross-check).
+"""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_block_scaled_group_amd import binding as B
+from nvfp4_block_scaled_group_amd import synth
+from oracle import oracle as O
+
+from gpu_helpers import Guarded, first_mismatch, log, run_host_split, to_device, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_columnwise_lines(q, splits, k):
+    """Oracle decode of the transposed output, in its own layout."""
+    out = np.empty(q["col_data"].size * 2, np.float32)
+    r0 = 0
+    for e, m in enumerate(splits):
+        for c in range(k if m else 0):
+            base = k * r0 + c * m
+            out[base: base + m] = O.decode_line(q["col_data"][base // 2: (base + m) // 2],
+                                                q["col_scale"][base // 16: (base + m) // 16], m,
+                                                q["col_amax"][e * k + c])
+        r0 += m
+    return out
+
+
+@pytest.mark.parametrize("splits,k,dist,seed", [
+    ([128, 0, 256, 128], 272, "rowscale", 71),
+    ([384, 128], 64, "outliers", 72),
+    ([128, 128], 48, "sparse", 73),
+])
+def test_dequant_matches_oracle_decode(splits, k, dist, seed):
+    w = synth.random_case(seed, splits, k, dist)
+    log(f"dequant {w.name} k={k}")
+    x = to_device(w.x)
+    g = to_numpy(run_host_split(x, splits))
+    t = {key: torch.from_numpy(np.ascontiguousarray(v)).cuda() for key, v in g.items()}
+    out_r = Guarded(4 * w.sum_m * k, torch.float32, (w.sum_m, k))
+    B.nvfp4_group_dequant_rowwise(t["row_data"], t["row_scale"], t["row_amax"], out_r.t)
+    out_c = Guarded(4 * w.sum_m * k, torch.float32)
+    B.nvfp4_group_dequant_columnwise(t["col_data"], t["col_scale"], t["col_amax"], splits, k, out_c.t)
+    torch.cuda.synchronize()
+    assert out_r.guards_intact() and out_c.guards_intact()
+    ref_r = O.decode_rowwise(g["row_data"], g["row_scale"], g["row_amax"])
+    assert first_mismatch(out_r.numpy(), ref_r) is None
+    ref_c = oracle_columnwise_lines(g, splits, k)
+    assert first_mismatch(out_c.numpy(), ref_c) is None
+
+
+def test_dequant_closed_form_reproduces_input():
+    rng = np.random.default_rng(74)
+    M, K = 256, 96
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    gv = grid[rng.integers(0, 8, (M, K))] * rng.choice([-1.0, 1.0], (M, K))
+    r, c = np.meshgrid(np.arange(M), np.arange(K), indexing="ij")
+    diag = (r % 16) == (c % 16)
+    gv[diag] = 6.0 * rng.choice([-1.0, 1.0], int(diag.sum()))
+    xf = (gv * 448.0 * 2.0 ** 3).astype(np.float32)
+    splits = [128, 128]
+    log("dequant closed form")
+    x = to_device(synth.f32_to_bf16_bits(xf))
+    g = to_numpy(run_host_split(x, splits))
+    t = {key: torch.from_numpy(np.ascontiguousarray(v)).cuda() for key, v in g.items()}
+    out_r = torch.empty((M, K), dtype=torch.float32, device="cuda:0")
+    B.nvfp4_group_dequant_rowwise(t["row_data"], t["row_scale"], t["row_amax"], out_r)
+    out_c = torch.empty(M * K, dtype=torch.float32, device="cuda:0")
+    B.nvfp4_group_dequant_columnwise(t["col_data"], t["col_scale"], t["col_amax"], splits, K, out_c)
+    torch.cuda.synchronize()
+    assert (out_r.cpu().numpy().view(np.uint32) == xf.view(np.uint32)).all()
+    xt = np.concatenate([np.ascontiguousarray(xf[0:128].T).reshape(-1), np.ascontiguousarray(xf[128:].T).reshape(-1)])
+    assert (out_c.cpu().numpy().view(np.uint32) == xt.view(np.uint32)).all()
+
+
+def test_dequant_columnwise_graphsafe_equals_host():
+    w = synth.random_case(75, [256, 0, 384], 80, "rowscale")
+    splits = list(map(int, w.splits))
+    log("dequant graph-safe")
+    x = to_device(w.x)
+    g = to_numpy(run_host_split(x, splits))
+    t = {key: torch.from_numpy(np.ascontiguousarray(v)).cuda() for key, v in g.items()}
+    a = torch.empty(w.sum_m * w.k, dtype=torch.float32, device="cuda:0")
+    B.nvfp4_group_dequant_columnwise(t["col_data"], t["col_scale"], t["col_amax"], splits, w.k, a)
+    b = torch.full((w.sum_m * w.k,), -7.0, dtype=torch.float32, device="cuda:0")
+    d_offs = torch.tensor(B.offsets_from_splits(splits), dtype=torch.int32, device="cuda:0")
+    d_status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    B.nvfp4_group_dequant_columnwise_graphsafe(t["col_data"], t["col_scale"], t["col_amax"], w.sum_m, w.k,
+                                               len(splits), d_offs, b, d_status)
+    torch.cuda.synchronize()
+    assert int(d_status.item()) == 0
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))

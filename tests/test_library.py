@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     assert _declared() == {
         "nvfp4_group_amax", "nvfp4_group_cast", "nvfp4_group_amax_graphsafe",
         "nvfp4_group_cast_graphsafe", "nvfp4_group_quantize", "nvfp4_group_quantize_graphsafe",
-        "nvfp4_group_strerror",
+        "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
+        "nvfp4_group_dequant_columnwise_graphsafe", "nvfp4_group_strerror",
     }
 
 
@@ -115,3 +116,18 @@ def test_graphsafe_static_checks(lib):
     assert f(FAKE, 200, 32, 2, FAKE, FAKE, FAKE, FAKE, None) == -1        # capacity not %128
     assert f(FAKE, 256, 32, 0, FAKE, FAKE, FAKE, FAKE, None) == -1        # no experts
     assert f(FAKE, 256, 32, 5000, FAKE, FAKE, FAKE, FAKE, None) == -1     # too many experts
+
+
+def test_dequant_host_checks(lib):
+    f = lib.nvfp4_group_dequant_rowwise
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(FAKE, FAKE, FAKE, 128, 24, FAKE, None) == -1       # k not a multiple of 16
+    assert f(None, FAKE, FAKE, 128, 32, FAKE, None) == -1       # missing input
+    assert f(FAKE, FAKE, FAKE, 128, 32, FAKE + 4, None) == -3   # misaligned output
+    g = lib.nvfp4_group_dequant_columnwise
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    sp = (ctypes.c_int64 * 2)(128, 100)
+    assert g(FAKE, FAKE, FAKE, 228, 32, 2, sp, FAKE, None) == -2  # split not a multiple of 128
