@@ -112,3 +112,22 @@ def group_quantize(x_bits, splits, rowwise=True, columnwise=True):
             r0 += m
         out.update(col_amax=ca, col_data=cd, col_scale=cs)
     return out
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def mx_encode_line(L):
+    """MXFP4 (OCP MX v1.0 reading): shared exponent floor(log2(block amax)) - 2
+    clamped to [-127, 127] (-127 for an all-zero block), E8M0 byte shared+127,
+    codes by nearest-value search over E2M1 of x / 2^shared."""
+    L = np.asarray(L, dtype=np.float32)
+    blocks = L.reshape(-1, 32).astype(np.float64)
+    A = np.abs(blocks).max(axis=1)
+    mant, ex = np.frexp(A)                        # A = mant * 2^ex, mant in [0.5, 1)
+    shared = np.where(A > 0, ex - 1 - 2, -127)
+    shared = np.clip(shared, -127, 127)
+    v = blocks / np.ldexp(1.0, shared)[:, None]   # exact in float64
+    mag = _nearest_even(E2M1, np.abs(v))
+    codes = (mag | (np.signbit(blocks).astype(np.int64) << 3)).reshape(-1)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    return packed, (shared + 127).astype(np.uint8)

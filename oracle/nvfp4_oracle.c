@@ -312,3 +312,103 @@ void oracle_block_scale_array(const float* b, const float* s, int64_t n,
                               int32_t* S_out, float* m_out) {
   for (int64_t i = 0; i < n; ++i) S_out[i] = oracle_block_scale(b[i], s[i], &m_out[i]);
 }
+
+/* ------------------------------------------------------------------ MXFP4
+ *
+ * The MXFP4 sibling format named on the TransformerEngine PR 3824 page
+ * (Changes item 1 and Testing: E2M1 elements, blocks of 32, E8M0
+ * power-of-two scales, the "pow_2_scales" branch).  The page gives no scale
+ * rule; the reading taken is the OCP Microscaling (MX) v1.0 definition: for
+ * a block with amax A,
+ *     shared = floor(log2(A)) - 2      (2 = exponent of FP4's largest value, 6 = 1.5 * 2^2)
+ *              clamped to [-127, 127]; -127 when A == 0
+ *     scale byte (E8M0) = shared + 127
+ *     element code = E2M1(x / 2^shared), nearest, ties to the even code,
+ *                    saturating at 6, sign of x kept.
+ * No amax pass and no line scale: every 32-block is independent.  Rowwise
+ * blocks run along the row, columnwise blocks along an expert's rows (the
+ * same transposed layout as NVFP4, with 1/32 instead of 1/16 scales).
+ */
+
+/* E8M0 byte of a block with amax A >= 0 (finite). */
+int oracle_mx_scale_byte(float A) {
+  if (!(A >= 0.0f)) return -1;
+  int shared = -127;
+  if (A > 0.0f) {
+    int ex;
+    frexp((double)A, &ex); /* A = f * 2^ex, f in [0.5, 1): floor(log2 A) = ex - 1 */
+    shared = ex - 1 - 2;
+    if (shared < -127) shared = -127;
+    if (shared > 127) shared = 127;
+  }
+  return shared + 127;
+}
+
+/* Encode one line of n values (n a multiple of 32). */
+int oracle_mx_encode_line(const float* L, int64_t n, uint8_t* codes, uint8_t* scales) {
+  if (n < 0 || n % 32 != 0) return ORACLE_EINVAL;
+  for (int64_t j = 0; j < n / 32; ++j) {
+    const float* blk = L + 32 * j;
+    float A = 0.0f;
+    for (int i = 0; i < 32; ++i) A = fmaxf(A, fabsf(blk[i]));
+    int byte = oracle_mx_scale_byte(A);
+    scales[j] = (uint8_t)byte;
+    double X = ldexp(1.0, byte - 127);
+    for (int i = 0; i < 32; i += 2) {
+      /* x / 2^shared is exact in double; as float it is exact for every
+         |value| >= 2^-126, and smaller ones all encode to a signed zero */
+      int c0 = oracle_e2m1_encode((float)((double)blk[i] / X));
+      int c1 = oracle_e2m1_encode((float)((double)blk[i + 1] / X));
+      codes[16 * j + i / 2] = (uint8_t)(c0 | (c1 << 4));
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Decode: value(code) * 2^(byte - 127), exact. */
+int oracle_mx_decode_line(const uint8_t* codes, const uint8_t* scales, int64_t n, float* out) {
+  if (n < 0 || n % 32 != 0) return ORACLE_EINVAL;
+  for (int64_t i = 0; i < n; ++i) {
+    int byte = codes[i / 2];
+    int code = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+    out[i] = (float)(oracle_e2m1_value(code) * ldexp(1.0, scales[i / 32] - 127));
+  }
+  return ORACLE_OK;
+}
+
+/* Grouped MXFP4 cast.  Rowwise: data [sum_m, k/2], scales [sum_m, k/32].
+ * Columnwise, expert e owning rows [r_e, r_e + M_e): data [k, M_e/2] at
+ * byte k*r_e/2, scales [k, M_e/32] at byte k*r_e/32.  k a multiple of 32;
+ * a direction is produced when its data pointer is non-NULL. */
+int oracle_mxfp4_group_cast(const uint16_t* x, int64_t sum_m, int64_t k, int32_t E,
+                            const int64_t* splits, uint8_t* row_data, uint8_t* row_scale,
+                            uint8_t* col_data, uint8_t* col_scale) {
+  int rc = check_args(sum_m, k, E, splits);
+  if (rc != ORACLE_OK || k % 32 != 0) return ORACLE_EINVAL;
+  float* L = (float*)malloc(sizeof(float) * (size_t)((k > sum_m ? k : sum_m) + 1));
+  if (!L) return ORACLE_EINVAL;
+  if (row_data) {
+    for (int64_t r = 0; r < sum_m && rc == ORACLE_OK; ++r) {
+      for (int64_t c = 0; c < k; ++c) L[c] = bf16_value(x[r * k + c]);
+      rc = oracle_mx_encode_line(L, k, row_data + r * (k / 2), row_scale + r * (k / 32));
+    }
+  }
+  if (col_data && rc == ORACLE_OK) {
+    int64_t r0 = 0;
+    for (int32_t e = 0; e < E && rc == ORACLE_OK; ++e) {
+      int64_t m = splits[e];
+      for (int64_t c = 0; c < k && rc == ORACLE_OK; ++c) {
+        for (int64_t r = 0; r < m; ++r) L[r] = bf16_value(x[(r0 + r) * k + c]);
+        rc = oracle_mx_encode_line(L, m, col_data + k * r0 / 2 + c * (m / 2),
+                                   col_scale + k * r0 / 32 + c * (m / 32));
+      }
+      r0 += m;
+    }
+  }
+  free(L);
+  return rc;
+}
+
+void oracle_mx_scale_byte_array(const float* A, int64_t n, int32_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_mx_scale_byte(A[i]);
+}

@@ -70,6 +70,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_e4m3_encode_array.argtypes = [_P, _I64, _P]
         L.oracle_e2m1_encode_array.argtypes = [_P, _I64, _P]
         L.oracle_block_scale_array.argtypes = [_P, _P, _I64, _P, _P]
+        L.oracle_mx_scale_byte.argtypes = [_F]
+        L.oracle_mx_scale_byte.restype = ctypes.c_int
+        L.oracle_mx_encode_line.argtypes = [_P, _I64, _P, _P]
+        L.oracle_mx_decode_line.argtypes = [_P, _P, _I64, _P]
+        L.oracle_mxfp4_group_cast.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P]
+        L.oracle_mx_scale_byte_array.argtypes = [_P, _I64, _P]
         _lib = L
     return _lib
 
@@ -233,3 +239,43 @@ def decode_columnwise(col_data, col_scale, col_amax, splits, k: int):
             out[r0:r0 + m, c] = decode_line(d[c], s[c], m, col_amax[e * k + c])
         r0 += m
     return out
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def mx_scale_byte(A: np.ndarray) -> np.ndarray:
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    out = np.empty(A.shape, dtype=np.int32)
+    lib().oracle_mx_scale_byte_array(_ptr(A), A.size, _ptr(out))
+    return out
+
+
+def mx_encode_line(L: np.ndarray):
+    L = np.ascontiguousarray(L, dtype=np.float32)
+    n = L.size
+    codes = np.empty(n // 2, dtype=np.uint8)
+    scales = np.empty(n // 32, dtype=np.uint8)
+    _check(lib().oracle_mx_encode_line(_ptr(L), n, _ptr(codes), _ptr(scales)), "mx_encode_line")
+    return codes, scales
+
+
+def mx_decode_line(codes, scales, n: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty(n, dtype=np.float32)
+    _check(lib().oracle_mx_decode_line(_ptr(codes), _ptr(scales), n, _ptr(out)), "mx_decode_line")
+    return out
+
+
+def mxfp4_group_cast(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool = True):
+    """Grouped MXFP4 cast: (row_data, row_scale, col_data, col_scale)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    sum_m, k = x.shape
+    sp = np.ascontiguousarray(splits, dtype=np.int64)
+    rd = np.empty((sum_m, k // 2), dtype=np.uint8) if rowwise else None
+    rs = np.empty((sum_m, k // 32), dtype=np.uint8) if rowwise else None
+    cd = np.empty(sum_m * k // 2, dtype=np.uint8) if columnwise else None
+    cs = np.empty(sum_m * k // 32, dtype=np.uint8) if columnwise else None
+    _check(lib().oracle_mxfp4_group_cast(_ptr(x), sum_m, k, sp.size, _ptr(sp), _ptr(rd), _ptr(rs), _ptr(cd),
+                                         _ptr(cs)), "mxfp4_group_cast")
+    return rd, rs, cd, cs
