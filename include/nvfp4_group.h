@@ -176,6 +176,40 @@ int nvfp4_group_dequant_columnwise_graphsafe(const uint8_t* col_data,
                                              const int32_t* d_offs, float* out,
                                              int32_t* d_status, void* stream);
 
+/* Grouped MXFP4 cast: the power-of-two-scaled sibling format named on the
+ * TransformerEngine PR 3824 page (Changes item 1, Testing): E2M1 elements,
+ * blocks of 32, one E8M0 scale byte per block.  The scale rule is the OCP
+ * Microscaling (MX) v1.0 one: for a block with amax A,
+ * shared = floor(log2 A) - 2 clamped to [-127, 127] (-127 for A == 0),
+ * byte = shared + 127, code = E2M1(x / 2^shared) (nearest, ties to even,
+ * saturating at 6, sign kept).  Each block is independent: no amax pass.
+ *
+ * x, sum_m, num_experts, h_splits as in nvfp4_group_cast; k > 0 and a
+ * multiple of 32 (else NVFP4G_EINVAL).  Outputs (caller-owned, 16-byte
+ * aligned; a direction is produced when its data pointer is non-NULL, and
+ * then needs its scale pointer):
+ *   row_data  [sum_m, k/2]   packed codes, element 2j in the low nibble
+ *   row_scale [sum_m, k/32]  E8M0 bytes
+ *   col_data  per expert e: [k, M_e/2] at byte k*r_e/2 (column c of expert
+ *             e packed along its rows)
+ *   col_scale per expert e: [k, M_e/32] at byte k*r_e/32
+ * Inputs must be finite.  Stream-ordered; allocates nothing. */
+int mxfp4_group_cast(const uint16_t* x, int64_t sum_m, int64_t k,
+                     int32_t num_experts, const int64_t* h_splits,
+                     uint8_t* row_data, uint8_t* row_scale, uint8_t* col_data,
+                     uint8_t* col_scale, void* stream);
+
+/* Graph-safe form of mxfp4_group_cast: routing from the device inclusive
+ * row ends d_offs[E] (as in nvfp4_group_cast_graphsafe); buffers sized for
+ * m_capacity rows; rows at or beyond offs[E-1] are not written; bad routing
+ * sets NVFP4G_DEV_* bits in *d_status and writes nothing. */
+int mxfp4_group_cast_graphsafe(const uint16_t* x, int64_t m_capacity,
+                               int64_t k, int32_t num_experts,
+                               const int32_t* d_offs, uint8_t* row_data,
+                               uint8_t* row_scale, uint8_t* col_data,
+                               uint8_t* col_scale, int32_t* d_status,
+                               void* stream);
+
 /* Static description of a status code. */
 const char* nvfp4_group_strerror(int status);
 

@@ -34,7 +34,7 @@ EXPORTS = (
     "nvfp4_group_amax", "nvfp4_group_cast", "nvfp4_group_amax_graphsafe",
     "nvfp4_group_cast_graphsafe", "nvfp4_group_quantize", "nvfp4_group_quantize_graphsafe",
     "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
-    "nvfp4_group_dequant_columnwise_graphsafe",
+    "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
     "nvfp4_group_strerror",
 )
 
@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.nvfp4_group_dequant_rowwise.argtypes = [_P, _P, _P, _I64, _I64, _P, _P]
     L.nvfp4_group_dequant_columnwise.argtypes = [_P, _P, _P, _I64, _I64, _I32, _P, _P, _P]
     L.nvfp4_group_dequant_columnwise_graphsafe.argtypes = [_P, _P, _P, _I64, _I64, _I32, _P, _P, _P, _P]
+    L.mxfp4_group_cast.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P]
+    L.mxfp4_group_cast_graphsafe.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = ctypes.c_int
     L.nvfp4_group_strerror.argtypes = [ctypes.c_int]
@@ -187,6 +189,21 @@ def nvfp4_group_dequant_columnwise_graphsafe(col_data, col_scale, col_amax, m_ca
                _ptr(d_offs), _ptr(out), _ptr(d_status), _stream(stream)))
 
 
+def mxfp4_group_cast(x, h_splits, row_data=None, row_scale=None, col_data=None, col_scale=None, stream=None):
+    xp, m, k = _x(x)
+    sp, e = _splits(h_splits)
+    _check("mxfp4_group_cast", load_library().mxfp4_group_cast(
+        xp, m, k, e, sp, _ptr(row_data), _ptr(row_scale), _ptr(col_data), _ptr(col_scale), _stream(stream)))
+
+
+def mxfp4_group_cast_graphsafe(x, num_experts, d_offs, d_status, row_data=None, row_scale=None, col_data=None,
+                               col_scale=None, stream=None):
+    xp, m, k = _x(x)
+    _check("mxfp4_group_cast_graphsafe", load_library().mxfp4_group_cast_graphsafe(
+        xp, m, k, int(num_experts), _ptr(d_offs), _ptr(row_data), _ptr(row_scale), _ptr(col_data),
+        _ptr(col_scale), _ptr(d_status), _stream(stream)))
+
+
 # ---------------------------------------------------------------- helpers
 
 def alloc_outputs(m_rows: int, k: int, num_experts: int, rowwise: bool = True, columnwise: bool = True,
@@ -202,6 +219,17 @@ def alloc_outputs(m_rows: int, k: int, num_experts: int, rowwise: bool = True, c
     if columnwise:
         out.update(col_amax=torch.empty(num_experts * k, **f32),
                    col_data=torch.empty(m_rows * k // 2, **u8), col_scale=torch.empty(m_rows * k // 16, **u8))
+    return out
+
+
+def alloc_mx_outputs(m_rows: int, k: int, rowwise: bool = True, columnwise: bool = True, device="cuda"):
+    """Allocate MXFP4 output buffers for ``m_rows`` rows (codes 2 per byte, one E8M0 byte per 32)."""
+    u8 = dict(dtype=torch.uint8, device=device)
+    out = {"row_data": None, "row_scale": None, "col_data": None, "col_scale": None}
+    if rowwise:
+        out.update(row_data=torch.empty((m_rows, k // 2), **u8), row_scale=torch.empty((m_rows, k // 32), **u8))
+    if columnwise:
+        out.update(col_data=torch.empty(m_rows * k // 2, **u8), col_scale=torch.empty(m_rows * k // 32, **u8))
     return out
 
 

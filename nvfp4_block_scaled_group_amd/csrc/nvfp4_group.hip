@@ -59,38 +59,6 @@ __global__ __launch_bounds__(kThreads) void amax_init_kernel(
   }
 }
 
-// Tile order of the cast kernel.  Work-groups are dispatched round-robin
-// over the 8 XCDs, each with its own L2; the linear block id is remapped so
-// that each XCD gets a contiguous run of logical tiles, ordered row tile
-// first within a 256-column chunk.  Vertically adjacent tiles, which write
-// the two 64-byte halves of each 128-byte line of the transposed output, then
-// go through the same L2 at about the same time.
-constexpr int kNumXcd = 8;
-
-struct TileCoord {
-  uint32_t row_tile, chunk;
-};
-
-__device__ __forceinline__ TileCoord tile_coord(uint32_t nrow_tiles) {
-  const uint32_t nb = gridDim.x, L = blockIdx.x;
-  const uint32_t xcd = L % kNumXcd, q = nb / kNumXcd, r = nb % kNumXcd;
-  const uint32_t lt = xcd * q + min(xcd, r) + L / kNumXcd;  // a permutation of 0..nb-1
-  return TileCoord{uni(lt % nrow_tiles), uni(lt / nrow_tiles)};
-}
-
-// Loads the lane's 16 rows x 8 columns (16 x 16 bytes) of a 128 x 256 tile
-// whose first element is `tile`; `vo` is the lane's byte offset (or
-// kOutOfRange), row i adds i*K*2 bytes as a scalar offset.
-__device__ __forceinline__ void load_tile(const uint16_t* tile, uint32_t ku, uint32_t vo,
-                                          uint32_t (&v)[16][4]) {
-  const rsrc_t xr = make_rsrc(tile);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, vo, (uint32_t)i * ku * 2u, kLoadStream);
-    v[i][0] = q.x; v[i][1] = q.y; v[i][2] = q.z; v[i][3] = q.w;
-  }
-}
-
 // Grouped amax, persistent: a grid of G workgroups, workgroup g walks the
 // contiguous range [g*T/G, (g+1)*T/G) of the T tiles of 64 rows x 512
 // columns, ordered row tile fastest within each 512-column chunk (so a
@@ -452,11 +420,6 @@ int check_cast_outputs(const float* row_amax, const float* col_amax, const uint8
 unsigned amax_grid(int64_t rows, int64_t k) {
   const int64_t tiles = (rows / kAmaxRows) * ((k + kAmaxCols - 1) / kAmaxCols);
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(tiles, NVFP4G_AMAX_WGS));
-}
-// 1-D grid of 128-row tiles x 256-column chunks for the cast kernel.
-uint32_t num_row_tiles(int64_t rows) { return (uint32_t)((rows + kTileRows - 1) / kTileRows); }
-dim3 tile_grid(int64_t rows, int64_t k) {
-  return dim3(num_row_tiles(rows) * (unsigned)((k + kTileCols - 1) / kTileCols));
 }
 
 int launch_amax(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, float* row_amax,

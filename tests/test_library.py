@@ -17,7 +17,7 @@ def _declared():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nvfp4_\w+)\s*\(", text, flags=re.M))
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:nv|mx)fp4_\w+)\s*\(", text, flags=re.M))
     return names
 
 
@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
         "nvfp4_group_amax", "nvfp4_group_cast", "nvfp4_group_amax_graphsafe",
         "nvfp4_group_cast_graphsafe", "nvfp4_group_quantize", "nvfp4_group_quantize_graphsafe",
         "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
-        "nvfp4_group_dequant_columnwise_graphsafe", "nvfp4_group_strerror",
+        "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
+        "nvfp4_group_strerror",
     }
 
 
@@ -131,3 +132,21 @@ def test_dequant_host_checks(lib):
                                           ctypes.c_void_p, ctypes.c_void_p]
     sp = (ctypes.c_int64 * 2)(128, 100)
     assert g(FAKE, FAKE, FAKE, 228, 32, 2, sp, FAKE, None) == -2  # split not a multiple of 128
+
+
+def test_mxfp4_host_checks(lib):
+    f = lib.mxfp4_group_cast
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 6
+    sp = (ctypes.c_int64 * 1)(128)
+    assert f(FAKE, 128, 48, 1, sp, FAKE, FAKE, None, None, None) == -1         # k not a multiple of 32
+    assert f(FAKE, 128, 64, 1, sp, FAKE, None, None, None, None) == -1         # rowwise data without scales
+    assert f(FAKE, 128, 64, 1, sp, None, None, FAKE, None, None) == -1         # columnwise data without scales
+    assert f(FAKE, 128, 64, 1, sp, FAKE, FAKE + 8, None, None, None) == -3     # misaligned scales
+    bad = (ctypes.c_int64 * 1)(100)
+    assert f(FAKE, 100, 64, 1, bad, FAKE, FAKE, None, None, None) == -2        # split not a multiple of 128
+    g = lib.mxfp4_group_cast_graphsafe
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 7
+    assert g(FAKE, 256, 64, 2, None, FAKE, FAKE, None, None, FAKE, None) == -1  # no device offsets
+    assert g(FAKE, 256, 64, 2, FAKE, FAKE, FAKE, None, None, None, None) == -1  # no status word
