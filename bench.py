@@ -12,6 +12,12 @@ value = algorithmic bytes per step / time per step, where the algorithmic
 bytes count what the method must move: two reads of x (the column amax needs
 every row of an expert before any of its blocks can be cast), the amax
 vectors written once and read once, and both outputs written once.
+
+On workloads with both directions the JSON line also carries ``next_rows``:
+the grouped MXFP4 cast of the same input (one read of x, both MXFP4 outputs
+written) and the rowwise / columnwise NVFP4 dequant of the step's outputs
+(codes, scales and line amax read once, fp32 written), each timed with HIP
+events over repeated launches.
 """
 from __future__ import annotations
 
@@ -75,6 +81,8 @@ def main():
                     choices=["deepseek_share", "down_proj", "outliers", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph-replays", type=int, default=100)
+    ap.add_argument("--next-rows", type=int, default=20,
+                    help="launches timed for each of the MXFP4 cast and the two dequants (0: skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (3 times, untimed) so that a "
                          "rocprofv3 --pmc run can scale FETCH_SIZE / WRITE_SIZE by a copy of known size")
@@ -179,6 +187,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if w.rowwise and w.columnwise and args.next_rows > 0:
+        result["next_rows"] = next_rows(B, torch, x, splits, out, E, k, m, args.next_rows)
+
     if args.workload == "deepseek_share" and args.graph_replays > 0:
         result["graph_replay"] = graph_replay(B, synth, torch, dev, args.graph_replays)
 
@@ -186,6 +197,42 @@ def main():
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)
+
+
+def next_rows(B, torch, x, splits, out, E: int, k: int, m: int, reps: int) -> dict:
+    """MXFP4 cast of the step's input and NVFP4 dequant of its outputs."""
+    print("[bench] MXFP4 cast and dequant", file=sys.stderr, flush=True)
+    N = m * k
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    def entry(kernel, ms, nbytes):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"kernel": kernel, "avg_us": round(ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes,
+                "GBps": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    res = {}
+    mx = B.alloc_mx_outputs(m, k, device=x.device)
+    ms = timed(lambda: B.mxfp4_group_cast(x, splits, **mx))
+    res["mxfp4_group_cast"] = entry("mxfp4_group_cast_kernel", ms, 2 * N + 2 * (N // 2 + N // 32))
+    del mx
+    deq = torch.empty(N, dtype=torch.float32, device=x.device)
+    ms = timed(lambda: B.nvfp4_group_dequant_rowwise(out["row_data"], out["row_scale"], out["row_amax"],
+                                                      deq.view(m, k)))
+    res["nvfp4_group_dequant_rowwise"] = entry("dequant_kernel", ms, N // 2 + N // 16 + 4 * m + 4 * N)
+    ms = timed(lambda: B.nvfp4_group_dequant_columnwise(out["col_data"], out["col_scale"], out["col_amax"],
+                                                         splits, k, deq))
+    res["nvfp4_group_dequant_columnwise"] = entry("dequant_kernel", ms, N // 2 + N // 16 + 4 * E * k + 4 * N)
+    return res
 
 
 def graph_replay(B, synth, torch, dev, replays: int) -> dict:

@@ -171,10 +171,22 @@ int check_mx(const void* x, int64_t rows, int64_t k, int32_t E, Routing* R, cons
   return NVFP4G_OK;
 }
 
+// Residency cap: at most two work-groups (two tiles in flight) per CU.  The
+// kernel needs 90 VGPRs (five waves per SIMD), but with that many tiles in
+// flight the interleaved row and transposed stores run the HBM slower: on
+// the 32-expert K=7168 sum_M=65536 workload one launch takes ~388 us
+// uncapped, ~355 us at three and ~325 us at two work-groups per CU (one is
+// slower again, ~399 us).  Reserving half of the CU's 160 KB of LDS per
+// work-group (dynamic LDS the kernel does not touch) enforces the cap.
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr int kMxGroupsPerCu = 2;
+constexpr size_t kMxStaticLds = kTileRows * (kTileCols / 128) * 4 + kTileCols * 4;  // l_rs + l_cs
+constexpr size_t kMxLdsReserve = kLdsPerCu / kMxGroupsPerCu - kMxStaticLds;
+
 int launch_mx(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, uint8_t* row_data,
               uint8_t* row_scale, uint8_t* col_data, uint8_t* col_scale, hipStream_t st) {
   if ((!row_data && !col_data) || rows == 0) return NVFP4G_OK;
-  hipLaunchKernelGGL(mxfp4_group_cast_kernel, tile_grid(rows, k), dim3(kThreads), 0, st, x, k, R,
+  hipLaunchKernelGGL(mxfp4_group_cast_kernel, tile_grid(rows, k), dim3(kThreads), kMxLdsReserve, st, x, k, R,
                      num_row_tiles(rows), row_data, row_scale, col_data, col_scale);
   return hip_status();
 }

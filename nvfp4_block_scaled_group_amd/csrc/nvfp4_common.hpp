@@ -35,6 +35,10 @@ struct Routing {
 // descriptors built from them, in scalar registers.
 __device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+  const uint32_t lo = uni((uint32_t)v), hi = uni((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Inclusive row end of expert e, for an e that is the same in every lane.
 __device__ __forceinline__ int32_t route_end(const Routing& R, int e) {

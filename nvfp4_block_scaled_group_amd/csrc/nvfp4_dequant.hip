@@ -13,9 +13,7 @@
 // Both outputs are laid out like the data they decode: element i of the
 // rowwise output (row i / K) or of the columnwise output (expert blocks of
 // [K, M_e] lines, concatenated in expert order) has its data nibble in byte
-// i/2 and its scale in byte i/16, and is written to out[i] (fp32).  One
-// thread decodes one 16-element block: an 8-byte data load, one scale byte,
-// one line amax, four 16-byte stores.
+// i/2 and its scale in byte i/16, and is written to out[i] (fp32).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,61 +24,91 @@ namespace {
 
 using namespace nvfp4g;
 
-// Value of a 4-bit E2M1 code: magnitudes 0, 0.5 for codes 0, 1; for codes
-// 2..7 the fp32 pattern with exponent (code >> 1) - 1 and mantissa bit code & 1.
-__device__ __forceinline__ float e2m1_value(uint32_t code) {
-  const uint32_t mag = code & 7u;
-  const float v = mag >= 2u ? __uint_as_float((((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22))
-                            : (float)mag * 0.5f;
-  return __uint_as_float(__float_as_uint(v) | ((code & 8u) << 28));
-}
+// Work unit: a chunk of 1024 consecutive output elements per wave.  Lane l
+// decodes the four elements 256g + 4l .. +3 of the chunk for g = 0..3, so
+// each of the wave's four 16-byte stores covers 1 KB of contiguous output.
+// A 16-element block (and so a line) never splits across a lane's group of
+// four.  In the columnwise layout expert e's span [K*r_e, K*r_{e+1}) is a
+// multiple of 2048 elements (r_e a multiple of 128, K of 16), so a chunk
+// lies in one expert: the expert search and the 64-bit division that
+// places the chunk on its first line are per chunk and wave-uniform.
+constexpr int kChunk = 1024;
 
-// Line-amax index of element i in the columnwise layout: expert e owns the
-// elements [K*r_e, K*r_{e+1}), line c = (i - K*r_e) / M_e.
-__device__ __forceinline__ int64_t col_line(const Routing& R, int64_t k, int64_t i) {
-  int lo = 0, hi = R.num_experts - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)route_end_lane(R, mid) * k > i) hi = mid; else lo = mid + 1;
+// Magnitudes of the E2M1 codes 0..7 in units of 0.5 (0 1 2 3 4 6 8 12),
+// one nibble each.
+constexpr uint32_t kE2m1Halves = 0xC8643210u;
+
+// value(code) * value(S) * s for the four codes of a 16-bit group, with
+// hS = value(S) / 2: n * hS is the exact product value(code) * value(S) (a
+// 4-bit integer times an E4M3 value), so the one rounding is the product
+// with s, as in (value(code) * value(S)) * s; the sign is applied last
+// (rounding to nearest is symmetric).
+__device__ __forceinline__ float4 decode4(uint32_t q, float hS, float s) {
+  float r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t c = (q >> (4 * j)) & 15u;
+    const float mag = (float)((kE2m1Halves >> ((c & 7u) * 4u)) & 15u) * hS;
+    r[j] = __uint_as_float(__float_as_uint(mag * s) | ((c & 8u) << 28));
   }
-  const int64_t rb = lo ? route_end_lane(R, lo - 1) : 0;
-  const int64_t me = route_end_lane(R, lo) - rb;
-  return (int64_t)lo * k + (i - k * rb) / me;
+  return make_float4(r[0], r[1], r[2], r[3]);
 }
 
-// columnwise = false: line = i / k (rowwise); true: col_line (needs R).
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t* __restrict__ data, const uint8_t* __restrict__ scale, const float* __restrict__ amax,
     int64_t k, int64_t n_elems, bool columnwise, Routing R, float* __restrict__ out) {
   if (columnwise && !routing_ok(R)) return;
   if (columnwise) n_elems = k * route_end(R, R.num_experts - 1);
-  const int64_t nblocks = n_elems / 16;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
-       b += (int64_t)gridDim.x * kThreads) {
-    const int64_t i = 16 * b;
-    const int64_t line = columnwise ? col_line(R, k, i) : i / k;
-    const float s = amax[line] / 2688.0f;
-    const float S = e4m3_value(scale[b]);
-    const uint2 q = *reinterpret_cast<const uint2*>(data + 8 * b);
-    float4 o[4];
-    float* f = reinterpret_cast<float*>(o);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t word = j < 8 ? q.x : q.y;
-      const uint32_t code = (word >> (4 * (j & 7))) & 15u;
-      f[j] = (e2m1_value(code) * S) * s;
+  const int64_t nchunks = (n_elems + kChunk - 1) / kChunk;
+  const uint32_t lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t c = uni((uint32_t)(blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6))); c < nchunks;
+       c += nwaves) {
+    const int64_t c0 = c * kChunk;
+    // the chunk's lines: element c0 + o lies on line  lbase + (rem0 + o) / len
+    int64_t lbase, rem0, len;
+    if (columnwise) {
+      int32_t rbeg, rend;
+      const int e = find_expert(R, (int32_t)(c0 / k), &rbeg, &rend);
+      len = rend - rbeg;
+      const int64_t t = c0 - k * rbeg;
+      lbase = (int64_t)e * k + t / len;
+      rem0 = t % len;
+    } else {
+      len = k;
+      lbase = c0 / k;
+      rem0 = c0 % k;
     }
-    float4* dst = reinterpret_cast<float4*>(out + i);
+    const uint32_t ulen = uni((uint32_t)len), urem = uni((uint32_t)rem0);
+    const float inv_len = 1.0f / (float)ulen;
+    const uint32_t left = (uint32_t)min<int64_t>(n_elems - c0, kChunk);  // elements of this chunk
+    const uint8_t* dch = data + c0 / 2;
+    const uint8_t* sch = scale + c0 / 16;
+    const float* ach = amax + uni(lbase);
+    float* och = out + c0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dst[j] = o[j];
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t o = 256u * g + 4u * lane;
+      if (o >= left) break;
+      // line offset (urem + o) / ulen: float estimate, then one correction
+      // step (the estimate is within 1 for quotients below 2^22)
+      const uint32_t v = urem + o;
+      uint32_t d = (uint32_t)((float)v * inv_len);
+      const int32_t rem = (int32_t)(v - d * ulen);
+      d = rem < 0 ? d - 1 : (rem >= (int32_t)ulen ? d + 1 : d);
+      const float s = ach[d] / 2688.0f;
+      const float hS = e4m3_value(sch[o / 16]) * 0.5f;
+      const uint32_t q = *reinterpret_cast<const uint16_t*>(dch + o / 2);
+      *reinterpret_cast<float4*>(och + o) = decode4(q, hS, s);
+    }
   }
 }
 
 int launch_dequant(const uint8_t* data, const uint8_t* scale, const float* amax, int64_t k, int64_t n_elems,
                    bool columnwise, const Routing& R, float* out, hipStream_t st) {
-  const int64_t nblocks = n_elems / 16;
-  if (nblocks == 0 && !columnwise) return NVFP4G_OK;
-  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((nblocks + kThreads - 1) / kThreads, 8192));
+  if (n_elems == 0) return NVFP4G_OK;
+  const int64_t waves = (n_elems + kChunk - 1) / kChunk;
+  const unsigned grid = (unsigned)std::min<int64_t>((waves + 3) / 4, 4096);
   hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kThreads), 0, st, data, scale, amax, k, n_elems, columnwise,
                      R, out);
   return hip_status();

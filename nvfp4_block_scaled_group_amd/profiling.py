@@ -8,9 +8,11 @@
 ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the same command
 with ``--calib-copy``, which adds a plain 1 GiB device copy.  FETCH_SIZE and
 WRITE_SIZE (KiB per dispatch) are scaled by what they read for that copy of
-known size (1 GiB read, 1 GiB written), giving HBM bytes per launch.  The
-summary records the SHA-256 of the HIP source it was measured on; the
-benchmark reports the traffic only while the source is unchanged.
+known size (1 GiB read, 1 GiB written), giving HBM bytes per launch.  Each
+kernel's entry records the SHA-256 of the sources it is built from (its .hip
+file and the shared headers); the benchmark reports a kernel's traffic only
+while those sources are unchanged.  ``--kernels`` limits a summary to some
+kernels (plus the calibration copy).
 """
 from __future__ import annotations
 
@@ -23,14 +25,29 @@ import os
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-SOURCE = os.path.join(PKG, "csrc", "nvfp4_group.hip")
+CSRC = os.path.join(PKG, "csrc")
 COPY_BYTES = 1 << 30
-KERNELS = ("group_cast_kernel", "group_amax_kernel", "amax_init_kernel", "group_quantize_rowwise_kernel")
+# kernel -> the .hip file that defines it; the longer names come first, since
+# names are matched as substrings of the profiler's kernel names
+KERNEL_SOURCES = {
+    "mxfp4_group_cast_kernel": "mxfp4_group.hip",
+    "group_cast_kernel": "nvfp4_group.hip",
+    "group_amax_kernel": "nvfp4_group.hip",
+    "amax_init_kernel": "nvfp4_group.hip",
+    "group_quantize_rowwise_kernel": "nvfp4_group.hip",
+    "dequant_kernel": "nvfp4_dequant.hip",
+}
+KERNELS = tuple(KERNEL_SOURCES)
 
 
-def source_sha256() -> str:
-    with open(SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha256(kernel: str) -> str:
+    """SHA-256 over the kernel's .hip file and every shared header."""
+    h = hashlib.sha256()
+    files = [KERNEL_SOURCES[kernel]] + sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def _short(name: str) -> str:
@@ -65,19 +82,20 @@ def counter(dirname: str, name: str) -> dict:
     return {k: statistics.median(v) for k, v in vals.items()}
 
 
-def summarize(stats_dir: str, fetch_dir: str, write_dir: str, cmd: str, workload: str) -> tuple[str, dict]:
-    st = kernel_stats(stats_dir)
-    fe = counter(fetch_dir, "FETCH_SIZE")
-    wr = counter(write_dir, "WRITE_SIZE")
+def summarize(stats_dir: str, fetch_dir: str, write_dir: str, cmd: str, workload: str,
+              kernels=None) -> tuple[str, dict]:
+    keep = (lambda k: True) if not kernels else (lambda k: k in kernels or k == "copy")
+    st = {k: v for k, v in kernel_stats(stats_dir).items() if keep(k)}
+    fe = {k: v for k, v in counter(fetch_dir, "FETCH_SIZE").items() if keep(k)}
+    wr = {k: v for k, v in counter(write_dir, "WRITE_SIZE").items() if keep(k)}
     fscale = COPY_BYTES / (fe["copy"] * 1024.0)
     wscale = COPY_BYTES / (wr["copy"] * 1024.0)
-    data = {"workload": workload, "source_sha256": source_sha256(), "fetch_scale": round(fscale, 4),
-            "write_scale": round(wscale, 4), "kernels": {}}
+    data = {"workload": workload, "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4), "kernels": {}}
     for k in sorted(set(fe) & set(wr)):
-        if k == "copy":
+        if k not in KERNEL_SOURCES:
             continue
         data["kernels"][k] = {"fetch_bytes": round(fe[k] * 1024 * fscale), "write_bytes": round(wr[k] * 1024 * wscale),
-                              "fetch_kib_raw": fe[k], "write_kib_raw": wr[k]}
+                              "fetch_kib_raw": fe[k], "write_kib_raw": wr[k], "source_sha256": source_sha256(k)}
     lines = [f"# rocprofv3 summary: {workload}", "",
              "Command (run from the repository root on one MI355X):", "",
              "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {cmd}",
@@ -94,7 +112,8 @@ def summarize(stats_dir: str, fetch_dir: str, write_dir: str, cmd: str, workload
     for k, v in data["kernels"].items():
         lines.append(f"| {k} | {v['fetch_kib_raw']:.0f} | {v['write_kib_raw']:.0f} | {v['fetch_bytes']} | "
                      f"{v['write_bytes']} |")
-    lines += ["", "Machine-readable (read by bench.py; valid only for the HIP source with this SHA-256):", "",
+    lines += ["", "Machine-readable (read by bench.py; a kernel's entry is valid only while its sources "
+              "have the SHA-256 it records):", "",
               "```json", json.dumps(data), "```", ""]
     return "\n".join(lines), data
 
@@ -111,9 +130,9 @@ def load_traffic(path: str, kernel: str):
         data = json.loads(block)
     except ValueError:
         return None
-    if data.get("source_sha256") != source_sha256() or kernel not in data.get("kernels", {}):
+    k = data.get("kernels", {}).get(kernel)
+    if k is None or kernel not in KERNEL_SOURCES or k.get("source_sha256") != source_sha256(kernel):
         return None
-    k = data["kernels"][kernel]
     return {"read_bytes": k["fetch_bytes"], "written_bytes": k["write_bytes"],
             "bytes": k["fetch_bytes"] + k["write_bytes"]}
 
@@ -126,8 +145,10 @@ def main():
     ap.add_argument("--cmd", required=True)
     ap.add_argument("--workload", default="deepseek_share_e32_k7168_m65536")
     ap.add_argument("--out", required=True)
+    ap.add_argument("--kernels", default="", help="comma-separated kernel names to keep (default: all)")
     a = ap.parse_args()
-    text, _ = summarize(a.stats, a.fetch, a.write, a.cmd, a.workload)
+    kernels = [k for k in a.kernels.split(",") if k] or None
+    text, _ = summarize(a.stats, a.fetch, a.write, a.cmd, a.workload, kernels)
     with open(a.out, "w") as f:
         f.write(text)
     print(text)

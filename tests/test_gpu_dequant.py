@@ -95,3 +95,47 @@ def test_dequant_columnwise_graphsafe_equals_host():
     torch.cuda.synchronize()
     assert int(d_status.item()) == 0
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("rows,k", [(37, 48), (1, 16), (129, 2064), (300, 272)])
+def test_dequant_rowwise_ragged_row_counts(rows, k):
+    # row counts that leave a partial last 1024-element chunk (or a single block)
+    w = synth.random_case(76 + rows, [((rows + 127) // 128) * 128], k, "outliers")
+    log(f"dequant rowwise rows={rows} k={k}")
+    g = to_numpy(run_host_split(to_device(w.x), list(map(int, w.splits)), True, False))
+    rd, rs, ra = (np.ascontiguousarray(g[key][:rows]) for key in ("row_data", "row_scale", "row_amax"))
+    out = Guarded(4 * rows * k, torch.float32, (rows, k))
+    B.nvfp4_group_dequant_rowwise(*(torch.from_numpy(v).cuda() for v in (rd, rs, ra)), out.t)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    assert first_mismatch(out.numpy(), O.decode_rowwise(rd, rs, ra)) is None
+
+
+def test_dequant_columnwise_many_small_experts_and_partial_routing():
+    # 20 experts of 128 rows at K=16: every expert spans two 1024-element
+    # chunks; the graph-safe call with capacity beyond the routed rows leaves
+    # the tail of the output untouched
+    splits = [128] * 20
+    k = 16
+    w = synth.random_case(77, splits, k, "rowscale")
+    log("dequant columnwise, 20 experts")
+    g = to_numpy(run_host_split(to_device(w.x), splits))
+    t = {key: torch.from_numpy(np.ascontiguousarray(v)).cuda() for key, v in g.items()}
+    out = Guarded(4 * w.sum_m * k, torch.float32)
+    B.nvfp4_group_dequant_columnwise(t["col_data"], t["col_scale"], t["col_amax"], splits, k, out.t)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    assert first_mismatch(out.numpy(), oracle_columnwise_lines(g, splits, k)) is None
+    part = splits[:13]
+    cap = w.sum_m
+    b = torch.full((cap * k,), -7.0, dtype=torch.float32, device="cuda:0")
+    d_offs = torch.tensor(B.offsets_from_splits(part), dtype=torch.int32, device="cuda:0")
+    d_status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    B.nvfp4_group_dequant_columnwise_graphsafe(t["col_data"], t["col_scale"], t["col_amax"], cap, k, len(part),
+                                               d_offs, b, d_status)
+    torch.cuda.synchronize()
+    assert int(d_status.item()) == 0
+    n = k * sum(part)
+    got = b.cpu().numpy()
+    assert first_mismatch(got[:n], out.numpy()[:n]) is None
+    assert (got[n:] == -7.0).all()
