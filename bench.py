@@ -22,6 +22,7 @@ events over repeated launches.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -35,6 +36,56 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "grouped NVFP4 amax+cast HBM GB/s (bytes in+out) and % of MI355X peak BW"
 TRAFFIC_FILE = "profiles/group_cast_kernel-deepseek_share_e32_k7168_m65536.md"
+
+
+class TimingEvents:
+    """HIP events for timing only, created with hipEventDisableSystemFence.
+
+    A default HIP event performs a system-scope fence when it is recorded
+    (a cache write-back and invalidate, which also slows the kernel that
+    follows); timing events need none of that: the host reads results only
+    after a device synchronisation.  Events are recorded on the stream the
+    library launches on (torch's current stream) through the HIP runtime
+    that torch has loaded."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, torch):
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.hip = ctypes.CDLL(path)
+        self.torch = torch
+        self.pool = []
+
+    def new(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.pool.append(ev)
+        return ev
+
+    def record(self, ev):
+        rc = self.hip.hipEventRecord(ev, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for ev in self.pool:
+            self.hip.hipEventDestroy(ev)
+        self.pool = []
 
 
 def algorithmic_bytes(sum_m: int, k: int, E: int, rowwise: bool, columnwise: bool) -> dict:
@@ -108,28 +159,30 @@ def main():
 
     fused = w.rowwise and not w.columnwise
 
+    tev = TimingEvents(torch)
+
     def step(ev=None):
         if ev is not None:
-            ev[0].record()
+            tev.record(ev[0])
         if fused:
             # rowwise only: one pass (row amax and cast together)
             B.nvfp4_group_quantize(x, splits, **out)
             if ev is not None:
-                ev[1].record()
-                ev[2].record()
+                tev.record(ev[1])
+                tev.record(ev[2])
             return
         B.nvfp4_group_amax(x, splits, out["row_amax"], out["col_amax"])
         if ev is not None:
-            ev[1].record()
+            tev.record(ev[1])
         B.nvfp4_group_cast(x, splits, **out)
         if ev is not None:
-            ev[2].record()
+            tev.record(ev[2])
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[tev.new() for _ in range(3)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -137,8 +190,8 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    first_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    second_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    first_ms = float(np.mean([tev.elapsed_ms(e[0], e[1]) for e in events]))
+    second_ms = float(np.mean([tev.elapsed_ms(e[1], e[2]) for e in events]))
     ms_per_step = wall * 1e3 / args.steps
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
     if fused:
@@ -188,18 +241,19 @@ def main():
         del src, dst
 
     if w.rowwise and w.columnwise and args.next_rows > 0:
-        result["next_rows"] = next_rows(B, torch, x, splits, out, E, k, m, args.next_rows)
+        result["next_rows"] = next_rows(B, torch, tev, x, splits, out, E, k, m, args.next_rows)
 
     if args.workload == "deepseek_share" and args.graph_replays > 0:
-        result["graph_replay"] = graph_replay(B, synth, torch, dev, args.graph_replays)
+        result["graph_replay"] = graph_replay(B, synth, torch, tev, dev, args.graph_replays)
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w)
+    tev.close()
     print(json.dumps(result), flush=True)
 
 
-def next_rows(B, torch, x, splits, out, E: int, k: int, m: int, reps: int) -> dict:
+def next_rows(B, torch, tev, x, splits, out, E: int, k: int, m: int, reps: int) -> dict:
     """MXFP4 cast of the step's input and NVFP4 dequant of its outputs."""
     print("[bench] MXFP4 cast and dequant", file=sys.stderr, flush=True)
     N = m * k
@@ -207,13 +261,13 @@ def next_rows(B, torch, x, splits, out, E: int, k: int, m: int, reps: int) -> di
     def timed(fn):
         fn()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        evs = [(tev.new(), tev.new()) for _ in range(reps)]
         for e0, e1 in evs:
-            e0.record()
+            tev.record(e0)
             fn()
-            e1.record()
+            tev.record(e1)
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return float(np.mean([tev.elapsed_ms(a, b) for a, b in evs]))
 
     def entry(kernel, ms, nbytes):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -235,7 +289,7 @@ def next_rows(B, torch, x, splits, out, E: int, k: int, m: int, reps: int) -> di
     return res
 
 
-def graph_replay(B, synth, torch, dev, replays: int) -> dict:
+def graph_replay(B, synth, torch, tev, dev, replays: int) -> dict:
     """Graph-safe path on the expert-share shapes with gradient-like values:
     one hipGraph capture of amax + cast, replayed with new routing written to
     the device offsets before each replay (the offset copy is outside the
@@ -262,13 +316,13 @@ def graph_replay(B, synth, torch, dev, replays: int) -> dict:
     times = []
     for i in range(replays):
         d_offs.copy_(routes[i], non_blocking=True)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e0, e1 = tev.new(), tev.new()
+        tev.record(e0)
         g.replay()
-        e1.record()
+        tev.record(e1)
         times.append((e0, e1))
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in times]))
+    ms = float(np.mean([tev.elapsed_ms(a, b) for a, b in times]))
     nbytes = algorithmic_bytes(m, k, E, True, True)["step"]
     return {"workload": w.name, "replays": replays, "ms_per_replay": round(ms, 4),
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 2), "status": int(d_status.item())}
