@@ -4,6 +4,9 @@ TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py``, never by the product package.  The
 oracle shares no code with the HIP library; see the header of
 ``nvfp4_oracle.c`` for what it computes and which page passages it follows.
+The row-scaled grouped GEMM at the end of this file (the cast's consumer) is
+plain numpy in float64 on top of the C oracle's two value tables; it is
+pinned by ``tests/test_oracle_gemm_pins.py``.
 """
 from __future__ import annotations
 
@@ -279,3 +282,95 @@ def mxfp4_group_cast(x: np.ndarray, splits, rowwise: bool = True, columnwise: bo
     _check(lib().oracle_mxfp4_group_cast(_ptr(x), sum_m, k, sp.size, _ptr(sp), _ptr(rd), _ptr(rs), _ptr(cd),
                                          _ptr(cs)), "mxfp4_group_cast")
     return rd, rs, cd, cs
+
+
+# ------------------------------------------------- row-scaled grouped GEMM
+#
+# The consumer of the cast ("Implement per-token NVFP4 fprop recipe",
+# TransformerEngine PR 2931, Greptile Summary and its sequence diagram: the
+# GEMM runs on the block-scaled FP4 operands with the row amax set aside, and
+# its fp32 output rows are then multiplied by the row amax; "[PyTorch] Enable
+# NVFP4 row-scaled (per-token) backward for GroupedLinear", TransformerEngine
+# PR 3324, Greptile Summary: the NT weight-gradient GEMM runs per expert on
+# the columnwise operands).  Here each operand element is dequantised in exact
+# arithmetic,  x = value(code) * value(S) * (A / 2688),  and the GEMM is the
+# plain product of the dequantised matrices.  It is evaluated in float64:
+# value(code) * value(S) is exact there, and a float64 dot product of
+# thousands of such terms is far more accurate than the fp32 result under
+# test.  The second return value is the same product taken over absolute
+# values, the scale of the rounding-error bound of an fp32 evaluation.
+
+def _values_table():
+    q = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+    s = np.array([e4m3_value(c) if c != 0x7F else np.nan for c in range(256)], dtype=np.float64)
+    return q, s
+
+
+def block_values(data: np.ndarray, scale: np.ndarray, n: int) -> np.ndarray:
+    """value(code) * value(S) for every element of `rows` lines of n elements:
+    data [rows, n/2] (element 2j in the low nibble of byte j), scale
+    [rows, n/16] E4M3 codes.  Exact in float64."""
+    q, s = _values_table()
+    data = np.asarray(data, dtype=np.uint8).reshape(-1, n // 2)
+    scale = np.asarray(scale, dtype=np.uint8).reshape(-1, n // 16)
+    codes = np.empty((data.shape[0], n), dtype=np.uint8)
+    codes[:, 0::2] = data & 15
+    codes[:, 1::2] = data >> 4
+    return q[codes] * np.repeat(s[scale], 16, axis=1)
+
+
+def _line_scales(amax) -> np.ndarray:
+    return np.asarray(amax, dtype=np.float32).astype(np.float64) / 2688.0
+
+
+def group_gemm(a_data, a_scale, a_amax, b_data, b_scale, b_amax, splits, n: int, k: int):
+    """Grouped row-scaled GEMM, forward form.  For expert e with rows
+    [r_e, r_e + M_e) of a:  out[r, j] = sum_t xa[r, t] * xb_e[j, t]  with
+    a = (a_data [sum_m, k/2], a_scale [sum_m, k/16], a_amax [sum_m]) and
+    b_e = (b_data [E, n, k/2], b_scale [E, n, k/16], b_amax [E*n]) row-scaled
+    NVFP4 operands.  Returns (out, bound_scale), both float64 [sum_m, n]."""
+    sp = [int(v) for v in splits]
+    sum_m = sum(sp)
+    E = len(sp)
+    a_vals = block_values(a_data, a_scale, k) if sum_m else np.zeros((0, k))
+    sa = _line_scales(a_amax)
+    b_vals = block_values(b_data, b_scale, k).reshape(E, n, k)
+    sb = _line_scales(b_amax).reshape(E, n)
+    out = np.zeros((sum_m, n), dtype=np.float64)
+    bound = np.zeros((sum_m, n), dtype=np.float64)
+    r0 = 0
+    for e, m in enumerate(sp):
+        if m:
+            A = a_vals[r0:r0 + m]
+            B = b_vals[e]
+            scale = np.outer(sa[r0:r0 + m], sb[e])
+            out[r0:r0 + m] = (A @ B.T) * scale
+            bound[r0:r0 + m] = (np.abs(A) @ np.abs(B).T) * np.abs(scale)
+        r0 += m
+    return out, bound
+
+
+def group_gemm_wgrad(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax,
+                     splits, n: int, k: int):
+    """Grouped row-scaled GEMM, weight-gradient form, on two columnwise
+    (transposed) cast outputs: a = dY's ([n, M_e] lines of expert e at byte
+    n*r_e/2, amax a_col_amax[e*n + i]) and b = X's ([k, M_e] lines, amax
+    b_col_amax[e*k + j]).  out[e, i, j] = sum_{t < M_e} xa_e[i, t] * xb_e[j, t],
+    i.e. dW_e = dY_e^T X_e; an expert without rows gets zeros.  Returns
+    (out, bound_scale), float64 [E, n, k]."""
+    sp = [int(v) for v in splits]
+    E = len(sp)
+    sa = _line_scales(a_col_amax).reshape(E, n)
+    sb = _line_scales(b_col_amax).reshape(E, k)
+    out = np.zeros((E, n, k), dtype=np.float64)
+    bound = np.zeros((E, n, k), dtype=np.float64)
+    r0 = 0
+    for e, m in enumerate(sp):
+        if m:
+            A = block_values(a_col_data[n * r0 // 2: n * (r0 + m) // 2], a_col_scale[n * r0 // 16: n * (r0 + m) // 16], m)
+            B = block_values(b_col_data[k * r0 // 2: k * (r0 + m) // 2], b_col_scale[k * r0 // 16: k * (r0 + m) // 16], m)
+            scale = np.outer(sa[e], sb[e])
+            out[e] = (A @ B.T) * scale
+            bound[e] = (np.abs(A) @ np.abs(B).T) * np.abs(scale)
+        r0 += m
+    return out, bound
