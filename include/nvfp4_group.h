@@ -210,6 +210,61 @@ int mxfp4_group_cast_graphsafe(const uint16_t* x, int64_t m_capacity,
                                uint8_t* col_scale, int32_t* d_status,
                                void* stream);
 
+/* Row-scaled NVFP4 grouped GEMM, the consumer of the cast ("Implement
+ * per-token NVFP4 fprop recipe", TransformerEngine PR 2931, Greptile Summary
+ * and sequence diagram: the GEMM runs on the block-scaled FP4 operands with
+ * the per-row amax set aside, produces fp32, and its rows are then
+ * multiplied by the row amax; grouped, one GEMM per expert).  Forward (and
+ * data-gradient) form, both operands stored along the contraction index k:
+ * for expert e and each of its rows r,
+ *     out[r, j] = sum_{t<k} xa[r, t] * xb_e[j, t],   j < n,
+ * where xa is the rowwise cast output (a_data [sum_m, k/2], a_scale
+ * [sum_m, k/16], a_amax [sum_m]) and xb_e is expert e's operand in the same
+ * rowwise layout (b_data [E, n, k/2], b_scale [E, n, k/16], b_amax [E*n]; a
+ * per-tensor-scaled operand is the case of a constant b_amax).  An element
+ * decodes to value(code) * value(S) * (A / 2688); the kernel computes
+ *     out = (acc * (a_amax[r] / 2688)) * (b_amax[e*n + j] / 2688)
+ * with acc the fp32 MFMA sum of the exact products value(code)*value(S)
+ * (fp16 operands).  For the data gradient pass the columnwise cast of each
+ * expert's weight as b.  out: fp32 [sum_m, n], row-major, caller-owned.
+ * k a positive multiple of 64 (<= 2^22), n a positive multiple of 16
+ * (<= 2^20); data pointers 16-byte aligned, scale and amax pointers 4-byte
+ * aligned; otherwise NVFP4G_EINVAL / NVFP4G_EALIGN and nothing is enqueued. */
+int nvfp4_group_gemm(const uint8_t* a_data, const uint8_t* a_scale,
+                     const float* a_amax, const uint8_t* b_data,
+                     const uint8_t* b_scale, const float* b_amax, int64_t sum_m,
+                     int64_t n, int64_t k, int32_t num_experts,
+                     const int64_t* h_splits, float* out, void* stream);
+
+/* Graph-safe form of nvfp4_group_gemm: routing from the device inclusive row
+ * ends d_offs[E] (as in nvfp4_group_cast_graphsafe); a and out hold
+ * m_capacity rows, of which rows at or beyond offs[E-1] are neither read nor
+ * written; bad routing sets NVFP4G_DEV_* bits in *d_status and writes
+ * nothing. */
+int nvfp4_group_gemm_graphsafe(const uint8_t* a_data, const uint8_t* a_scale,
+                               const float* a_amax, const uint8_t* b_data,
+                               const uint8_t* b_scale, const float* b_amax,
+                               int64_t m_capacity, int64_t n, int64_t k,
+                               int32_t num_experts, const int32_t* d_offs,
+                               float* out, int32_t* d_status, void* stream);
+
+/* Weight-gradient form ("[PyTorch] Enable NVFP4 row-scaled (per-token)
+ * backward for GroupedLinear", TransformerEngine PR 3324, Greptile Summary:
+ * an NT GEMM per expert on the columnwise operands, each with a per-column
+ * amax): with a = the columnwise cast of dY (per expert [n, M_e] lines at byte
+ * n*r_e/2, scales at n*r_e/16, amax a_col_amax[e*n + i]) and b = the
+ * columnwise cast of X (per expert [k, M_e] lines, amax b_col_amax[e*k + j]),
+ *     out[e, i, j] = sum_{r in expert e} xa_e[i, r] * xb_e[j, r]
+ * (dW_e = dY_e^T X_e), computed as in nvfp4_group_gemm; an expert without
+ * rows gets zeros.  out: fp32 [E, n, k].  n and k positive multiples of 16
+ * (<= 2^20). */
+int nvfp4_group_gemm_wgrad(const uint8_t* a_col_data, const uint8_t* a_col_scale,
+                           const float* a_col_amax, const uint8_t* b_col_data,
+                           const uint8_t* b_col_scale, const float* b_col_amax,
+                           int64_t sum_m, int64_t n, int64_t k,
+                           int32_t num_experts, const int64_t* h_splits,
+                           float* out, void* stream);
+
 /* Static description of a status code. */
 const char* nvfp4_group_strerror(int status);
 

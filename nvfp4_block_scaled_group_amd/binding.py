@@ -35,6 +35,7 @@ EXPORTS = (
     "nvfp4_group_cast_graphsafe", "nvfp4_group_quantize", "nvfp4_group_quantize_graphsafe",
     "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
     "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
+    "nvfp4_group_gemm", "nvfp4_group_gemm_graphsafe", "nvfp4_group_gemm_wgrad",
     "nvfp4_group_strerror",
 )
 
@@ -69,6 +70,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.nvfp4_group_dequant_columnwise_graphsafe.argtypes = [_P, _P, _P, _I64, _I64, _I32, _P, _P, _P, _P]
     L.mxfp4_group_cast.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P]
     L.mxfp4_group_cast_graphsafe.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
+    L.nvfp4_group_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P]
+    L.nvfp4_group_gemm_graphsafe.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P]
+    L.nvfp4_group_gemm_wgrad.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = ctypes.c_int
     L.nvfp4_group_strerror.argtypes = [ctypes.c_int]
@@ -202,6 +206,39 @@ def mxfp4_group_cast_graphsafe(x, num_experts, d_offs, d_status, row_data=None, 
     _check("mxfp4_group_cast_graphsafe", load_library().mxfp4_group_cast_graphsafe(
         xp, m, k, int(num_experts), _ptr(d_offs), _ptr(row_data), _ptr(row_scale), _ptr(col_data),
         _ptr(col_scale), _ptr(d_status), _stream(stream)))
+
+
+def nvfp4_group_gemm(a_data, a_scale, a_amax, b_data, b_scale, b_amax, h_splits, out, stream=None):
+    """Forward form: a_data [sum_m, k/2], a_scale [sum_m, k/16], a_amax [sum_m];
+    b_data [E, n, k/2], b_scale [E, n, k/16], b_amax [E*n] -> out f32 [sum_m, n]."""
+    sum_m, half_k = a_data.shape
+    E, n = b_data.shape[0], b_data.shape[1]
+    sp, e = _splits(h_splits)
+    if e != E:
+        raise ValueError(f"{e} splits for {E} expert operands")
+    _check("nvfp4_group_gemm", load_library().nvfp4_group_gemm(
+        _ptr(a_data), _ptr(a_scale), _ptr(a_amax), _ptr(b_data), _ptr(b_scale), _ptr(b_amax), sum_m, n,
+        2 * half_k, e, sp, _ptr(out), _stream(stream)))
+
+
+def nvfp4_group_gemm_graphsafe(a_data, a_scale, a_amax, b_data, b_scale, b_amax, d_offs, out, d_status,
+                               stream=None):
+    m_capacity, half_k = a_data.shape
+    E, n = b_data.shape[0], b_data.shape[1]
+    _check("nvfp4_group_gemm_graphsafe", load_library().nvfp4_group_gemm_graphsafe(
+        _ptr(a_data), _ptr(a_scale), _ptr(a_amax), _ptr(b_data), _ptr(b_scale), _ptr(b_amax), m_capacity, n,
+        2 * half_k, E, _ptr(d_offs), _ptr(out), _ptr(d_status), _stream(stream)))
+
+
+def nvfp4_group_gemm_wgrad(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax, h_splits,
+                           n, k, out, stream=None):
+    """Weight-gradient form on two columnwise cast outputs (dY's with n lines
+    per expert, X's with k) -> out f32 [E, n, k]."""
+    sp, e = _splits(h_splits)
+    sum_m = sum(int(v) for v in h_splits)
+    _check("nvfp4_group_gemm_wgrad", load_library().nvfp4_group_gemm_wgrad(
+        _ptr(a_col_data), _ptr(a_col_scale), _ptr(a_col_amax), _ptr(b_col_data), _ptr(b_col_scale),
+        _ptr(b_col_amax), sum_m, int(n), int(k), e, sp, _ptr(out), _stream(stream)))
 
 
 # ---------------------------------------------------------------- helpers

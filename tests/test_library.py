@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
         "nvfp4_group_cast_graphsafe", "nvfp4_group_quantize", "nvfp4_group_quantize_graphsafe",
         "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
         "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
+        "nvfp4_group_gemm", "nvfp4_group_gemm_graphsafe", "nvfp4_group_gemm_wgrad",
         "nvfp4_group_strerror",
     }
 
@@ -150,3 +151,32 @@ def test_mxfp4_host_checks(lib):
     g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 7
     assert g(FAKE, 256, 64, 2, None, FAKE, FAKE, None, None, FAKE, None) == -1  # no device offsets
     assert g(FAKE, 256, 64, 2, FAKE, FAKE, FAKE, None, None, None, None) == -1  # no status word
+
+
+def test_gemm_host_checks(lib):
+    f = lib.nvfp4_group_gemm
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 3 + [ctypes.c_int32, ctypes.c_void_p,
+                                                                   ctypes.c_void_p, ctypes.c_void_p]
+    sp = (ctypes.c_int64 * 2)(128, 128)
+    ok = [FAKE] * 6
+    assert f(*ok, 256, 32, 96, 2, sp, FAKE, None) == -1            # k not a multiple of 64
+    assert f(*ok, 256, 24, 128, 2, sp, FAKE, None) == -1           # n not a multiple of 16
+    assert f(*ok, 256, 0, 128, 2, sp, FAKE, None) == -1            # n = 0
+    assert f(*ok, 256, 32, 128, 2, sp, None, None) == -1           # no output
+    assert f(FAKE, FAKE, None, FAKE, FAKE, FAKE, 256, 32, 128, 2, sp, FAKE, None) == -1  # no row amax
+    assert f(FAKE + 8, *ok[1:], 256, 32, 128, 2, sp, FAKE, None) == -3                   # misaligned data
+    assert f(*ok, 256, 32, 128, 2, sp, FAKE + 2, None) == -3       # misaligned output
+    bad = (ctypes.c_int64 * 2)(128, 100)
+    assert f(*ok, 228, 32, 128, 2, bad, FAKE, None) == -2          # split not a multiple of 128
+    g = lib.nvfp4_group_gemm_graphsafe
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 3 + [ctypes.c_int32] + [ctypes.c_void_p] * 4
+    assert g(*ok, 256, 32, 128, 2, None, FAKE, FAKE, None) == -1   # no device offsets
+    assert g(*ok, 200, 32, 128, 2, FAKE, FAKE, FAKE, None) == -1   # capacity not a multiple of 128
+    w = lib.nvfp4_group_gemm_wgrad
+    w.restype = ctypes.c_int
+    w.argtypes = f.argtypes
+    assert w(*ok, 256, 24, 32, 2, sp, FAKE, None) == -1            # n not a multiple of 16
+    assert w(*ok, 256, 32, 40, 2, sp, FAKE, None) == -1            # k not a multiple of 16
+    assert w(*ok, 228, 32, 32, 2, bad, FAKE, None) == -2           # split not a multiple of 128
