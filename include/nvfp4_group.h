@@ -257,7 +257,7 @@ int nvfp4_group_gemm_graphsafe(const uint8_t* a_data, const uint8_t* a_scale,
  *     out[e, i, j] = sum_{r in expert e} xa_e[i, r] * xb_e[j, r]
  * (dW_e = dY_e^T X_e), computed as in nvfp4_group_gemm; an expert without
  * rows gets zeros.  out: fp32 [E, n, k].  n and k positive multiples of 16
- * (<= 2^20). */
+ * (<= 2^20); at most 2^22 rows per expert. */
 int nvfp4_group_gemm_wgrad(const uint8_t* a_col_data, const uint8_t* a_col_scale,
                            const float* a_col_amax, const uint8_t* b_col_data,
                            const uint8_t* b_col_scale, const float* b_col_amax,

@@ -25,18 +25,20 @@
 // besides the three fp32 operations of the epilogue.
 //
 // Design:
-//  * Work-group tile 128 (i) x 256 (j), 4 wave64s each computing 64 x 128 with
-//    2 x 4 v_mfma_f32_32x32x16_f16; the contraction advances 64 at a time.
-//  * Per step each thread loads raw FP4 bytes and E4M3 scale bytes (buffer
-//    loads: rows beyond the operand read as zero), decodes them with
-//    v_cvt_scalef32_pk_f16_fp4 (scale 1: the exact E2M1 values, two per
-//    instruction) and one packed fp16 multiply by value(S) per pair, and
-//    stores fp16 rows to LDS (row pitch 144 bytes: 16-byte fragment reads of
-//    8 consecutive rows hit distinct banks).  The next step's raw bytes are
-//    loaded while the MFMAs of the current step run.
-//  * Tile order: work-group ids are remapped so each XCD (own L2) gets a
-//    contiguous run of tiles, and inside it groups of 8 row tiles sweep the
-//    column tiles together, so A and B slices are shared through L2.
+//  * Work-group tile 128 (i) x 512 (j); 4 wave64s side by side along j, each
+//    computing 128 x 128 with 4 x 4 v_mfma_f32_32x32x16_f16 (256 fp32
+//    accumulators per lane, held in AGPRs); the contraction advances 64
+//    elements per step.
+//  * LDS holds the raw step: FP4 bytes and E4M3 scale bytes of the A and B
+//    lines (double-buffered; the next step is loaded into registers while
+//    the current one is multiplied).  Each wave decodes its own fragments
+//    right before the MFMAs: v_cvt_scalef32_pk_f16_fp4 with unit scale gives
+//    the exact E2M1 values two at a time, one packed fp16 multiply applies
+//    value(S) (converted once per block pair by v_cvt_scalef32_pk_f16_fp8).
+//  * Global loads are buffer loads: lines beyond an operand read as zero.
+//  * Tile order: groups of 8 row tiles sweep the column tiles together, and
+//    super-tiles of 64 tiles are dealt round-robin to the 8 XCDs, so each XCD
+//    shares operand slices through its L2 and the XCDs share the work evenly.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,10 +54,13 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;            // tile rows (i)
-constexpr int kBN = 256;            // tile columns (j)
+constexpr int kWavesM = 1, kWavesN = 4;  // wave grid of a work-group
+constexpr int kWM = 4, kWN = 4;          // 32 x 32 MFMA tiles per wave (i, j)
+constexpr int kBM = kWavesM * kWM * 32;  // tile rows (i): 128
+constexpr int kBN = kWavesN * kWN * 32;  // tile columns (j): 512
+static_assert(kBM == 128, "row tiles must be the 128-row expert granule");
+static_assert(kBN % kThreads == 0, "each thread copies whole B lines");
 constexpr int kBK = 64;             // contraction step
-constexpr int kPitch = kBK + 8;     // fp16 per LDS row (144 bytes)
 constexpr int kGroupRows = 8;       // row tiles per column sweep
 
 // One NT operand tile: `rows` lines of length L starting at the tile's first
@@ -66,12 +71,18 @@ struct OperandTile {
   uint32_t valid;        // lines that exist
 };
 
-// Logical tile index: each XCD gets a contiguous run (work-groups are
-// dispatched round-robin over the 8 XCDs).
-__device__ __forceinline__ uint32_t xcd_logical_id() {
-  const uint32_t nb = gridDim.x, L = blockIdx.x;
-  const uint32_t xcd = L % kNumXcd, q = nb / kNumXcd, r = nb % kNumXcd;
-  return uni(xcd * q + min(xcd, r) + L / kNumXcd);
+// Logical tile of this work-group.  Work-group i runs on XCD i % 8 (each
+// XCD has its own L2).  Super-tiles of 64 consecutive logical tiles are dealt
+// round-robin to the XCDs, so each XCD works through whole super-tiles
+// (whose operand slices its L2 shares) and the XCDs share the work evenly
+// even when tiles differ in cost (the weight-gradient tiles of a large expert
+// are longer).  Work-groups past the last full round keep their index.
+__device__ __forceinline__ uint32_t xcd_supertile_id() {
+  const uint32_t id = blockIdx.x, T = gridDim.x;
+  const uint32_t round = kNumXcd * 64, full = (T / round) * round;
+  if (id >= full) return uni(id);
+  const uint32_t j = id / kNumXcd, x = id % kNumXcd;
+  return uni((kNumXcd * (j / 64) + x) * 64 + j % 64);
 }
 
 // Grouped order inside `ntm` x `ntn` tiles: groups of kGroupRows row tiles
@@ -83,81 +94,121 @@ __device__ __forceinline__ void grouped_tile(uint32_t t, uint32_t ntm, uint32_t 
   *tn = uni(in / gm);
 }
 
-// fp16 value of an E4M3 code (exact).
-__device__ __forceinline__ _Float16 scale_h(uint32_t code) { return (_Float16)e4m3_value(code & 0xFFu); }
+// LDS stage: raw FP4 bytes and E4M3 scale bytes of one contraction step,
+// [line][32 bytes] codes and [line][4 bytes] scales for A then B.
+constexpr uint32_t kStA = 0, kStB = kBM * 32, kStAS = kStB + kBN * 32, kStBS = kStAS + kBM * 4;
+constexpr uint32_t kStageBytes = kStBS + kBN * 4;
 
-// Decode 8 bytes (16 codes of one block) scaled by value(S) into 16 fp16.
-__device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, _Float16 s, h8_t* lo, h8_t* hi) {
-  const h2_t ss = {s, s};
-#define NVFP4G_CVT(w, b) (__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w), 1.0f, (b)) * ss)
-  const h2_t p[8] = {NVFP4G_CVT(w0, 0), NVFP4G_CVT(w0, 1), NVFP4G_CVT(w0, 2), NVFP4G_CVT(w0, 3),
-                     NVFP4G_CVT(w1, 0), NVFP4G_CVT(w1, 1), NVFP4G_CVT(w1, 2), NVFP4G_CVT(w1, 3)};
-#undef NVFP4G_CVT
-  *lo = h8_t{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
-  *hi = h8_t{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+// Two E4M3 codes (low byte first) -> their fp16 values (exact: the fp8
+// convert with unit scale).
+__device__ __forceinline__ h2_t scales_h2(uint32_t two_codes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two_codes, 1.0f, false);
 }
 
-// acc[im][in] += A[64 rows of wave] x B[128 rows of wave]^T over the whole
-// contraction length L (a multiple of kBK).
-__device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTile& B, uint32_t L,
-                                          f32x16 (&acc)[2][4], _Float16* la, _Float16* lb) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t dpitch = L / 2, spitch = L / 16;
-  // A: thread -> line tid/2, half (tid&1) of the 64-element step (16 bytes)
-  const uint32_t a_line = tid >> 1, a_half = tid & 1;
-  const rsrc_t ad = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A.data), 0, A.valid * dpitch, 0x00020000);
-  const rsrc_t as = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A.scale), 0, A.valid * spitch, 0x00020000);
-  const uint32_t a_doff = a_line * dpitch + 16u * a_half, a_soff = a_line * spitch + 2u * a_half;
-  // B: thread -> line tid (32 bytes)
-  const rsrc_t bd = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(B.data), 0, B.valid * dpitch, 0x00020000);
-  const rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(B.scale), 0, B.valid * spitch, 0x00020000);
-  const uint32_t b_doff = (uint32_t)tid * dpitch, b_soff = (uint32_t)tid * spitch;
+// One MFMA operand fragment: the 8 codes of `w` (element 2j in the low
+// nibble of byte j) times value(S), as 8 fp16.
+__device__ __forceinline__ h8_t decode8(uint32_t w, _Float16 S) {
+  const h2_t ss = {S, S};
+  const h2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const h2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const h2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const h2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  return h8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
 
-  u32x4 ra, rb0, rb1;
-  uint32_t ras, rbs;
+// acc[im][in] += A[64 lines of the wave] x B[128 lines of the wave]^T over
+// the contraction length L (a multiple of kBK).
+//
+// Contraction order: the MFMA's 16 k-slots of sub-step s are, for lanes
+// 0-31 (h = 0) and 32-63 (h = 1), the 8 elements of byte word 4h + s of the
+// line's 32-byte step chunk.  A and B use the same assignment, so the sum is
+// the same; it lets each lane fetch its words of all four sub-steps with one
+// 16-byte LDS read, and its two block scales (blocks 2h, 2h+1) with one
+// 2-byte read.  LDS holds raw FP4 (double-buffered); each wave decodes its
+// own fragments right before the MFMAs.
+__device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTile& B, uint32_t L,
+                                          f32x16 (&acc)[kWM][kWN], uint8_t* lds) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // every descriptor field is work-group uniform: keep them in scalar registers
+  const uint32_t dpitch = uni(L / 2), spitch = uni(L / 16);
+  const uint32_t av = uni(A.valid), bv = uni(B.valid);
+  auto rsrc = [](const uint8_t* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(uni(reinterpret_cast<int64_t>(p))), 0, bytes, 0x00020000);
+  };
+  const rsrc_t ad = rsrc(A.data, av * dpitch), as = rsrc(A.scale, av * spitch);
+  const rsrc_t bd = rsrc(B.data, bv * dpitch), bs = rsrc(B.scale, bv * spitch);
+  // copy roles: A codes 16 bytes (line tid/2, half tid&1), A scales 4 bytes
+  // (line tid, threads < 128), B codes 32 bytes and B scales 4 bytes (line tid)
+  const uint32_t a_doff = (uint32_t)(tid >> 1) * dpitch + 16u * (tid & 1);
+  const uint32_t a_soff = tid < kBM ? (uint32_t)tid * spitch : kOutOfRange;
+  constexpr int kBL = kBN / kThreads;  // B lines copied per thread: tid + kThreads * c
+  u32x4 ra, rb[kBL][2];
+  uint32_t ras = 0, rbs[kBL];
   auto load = [&](uint32_t ks) {
     ra = __builtin_amdgcn_raw_buffer_load_b128(ad, a_doff, ks * 32u, 0);
-    ras = __builtin_amdgcn_raw_buffer_load_b16(as, a_soff, ks * 4u, 0);
-    rb0 = __builtin_amdgcn_raw_buffer_load_b128(bd, b_doff, ks * 32u, 0);
-    rb1 = __builtin_amdgcn_raw_buffer_load_b128(bd, b_doff + 16u, ks * 32u, 0);
-    rbs = __builtin_amdgcn_raw_buffer_load_b32(bs, b_soff, ks * 4u, 0);
+    if (tid < kBM) ras = __builtin_amdgcn_raw_buffer_load_b32(as, a_soff, ks * 4u, 0);
+#pragma unroll
+    for (int c = 0; c < kBL; ++c) {
+      const uint32_t line = (uint32_t)(tid + kThreads * c);
+      rb[c][0] = __builtin_amdgcn_raw_buffer_load_b128(bd, line * dpitch, ks * 32u, 0);
+      rb[c][1] = __builtin_amdgcn_raw_buffer_load_b128(bd, line * dpitch + 16u, ks * 32u, 0);
+      rbs[c] = __builtin_amdgcn_raw_buffer_load_b32(bs, line * spitch, ks * 4u, 0);
+    }
+  };
+  auto store = [&](uint32_t st) {
+    uint8_t* base = lds + st * kStageBytes;
+    *reinterpret_cast<u32x4*>(base + kStA + 16 * tid) = ra;
+    if (tid < kBM) *reinterpret_cast<uint32_t*>(base + kStAS + 4 * tid) = ras;
+#pragma unroll
+    for (int c = 0; c < kBL; ++c) {
+      const int line = tid + kThreads * c;
+      *reinterpret_cast<u32x4*>(base + kStB + 32 * line) = rb[c][0];
+      *reinterpret_cast<u32x4*>(base + kStB + 32 * line + 16) = rb[c][1];
+      *reinterpret_cast<uint32_t*>(base + kStBS + 4 * line) = rbs[c];
+    }
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN, h = lane >> 5;
   const uint32_t nk = L / kBK;
-  if (nk) load(0);
+  if (nk == 0) return;
+  load(0);
+  store(0);
+  if (nk > 1) load(1);
+  __syncthreads();
 #pragma unroll 1
   for (uint32_t ks = 0; ks < nk; ++ks) {
-    {
-      h8_t q0, q1, q2, q3;
-      decode_block(ra.x, ra.y, scale_h(ras), &q0, &q1);
-      decode_block(ra.z, ra.w, scale_h(ras >> 8), &q2, &q3);
-      h8_t* dst = reinterpret_cast<h8_t*>(la + a_line * kPitch + 32 * a_half);
-      dst[0] = q0; dst[1] = q1; dst[2] = q2; dst[3] = q3;
-      h8_t r0, r1, r2, r3, r4, r5, r6, r7;
-      decode_block(rb0.x, rb0.y, scale_h(rbs), &r0, &r1);
-      decode_block(rb0.z, rb0.w, scale_h(rbs >> 8), &r2, &r3);
-      decode_block(rb1.x, rb1.y, scale_h(rbs >> 16), &r4, &r5);
-      decode_block(rb1.z, rb1.w, scale_h(rbs >> 24), &r6, &r7);
-      h8_t* dstb = reinterpret_cast<h8_t*>(lb + tid * kPitch);
-      dstb[0] = r0; dstb[1] = r1; dstb[2] = r2; dstb[3] = r3;
-      dstb[4] = r4; dstb[5] = r5; dstb[6] = r6; dstb[7] = r7;
+    const uint32_t cur = ks & 1;
+    if (ks + 1 < nk) {
+      store(cur ^ 1);
+      if (ks + 2 < nk) load(ks + 2);
     }
-    __syncthreads();
-    if (ks + 1 < nk) load(ks + 1);
+    const uint8_t* base = lds + cur * kStageBytes;
+    u32x4 wa[kWM], wb[kWN];
+    h2_t sa[kWM], sb[kWN];
+#pragma unroll
+    for (int im = 0; im < kWM; ++im) {
+      const uint32_t line = wm * (kWM * 32) + im * 32 + (lane & 31);
+      wa[im] = *reinterpret_cast<const u32x4*>(base + kStA + 32 * line + 16 * h);
+      sa[im] = scales_h2(*reinterpret_cast<const uint16_t*>(base + kStAS + 4 * line + 2 * h));
+    }
+#pragma unroll
+    for (int in = 0; in < kWN; ++in) {
+      const uint32_t line = wn * (kWN * 32) + in * 32 + (lane & 31);
+      wb[in] = *reinterpret_cast<const u32x4*>(base + kStB + 32 * line + 16 * h);
+      sb[in] = scales_h2(*reinterpret_cast<const uint16_t*>(base + kStBS + 4 * line + 2 * h));
+    }
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      h8_t af[2], bf[4];
+      h8_t af[kWM], bf[kWN];
 #pragma unroll
-      for (int im = 0; im < 2; ++im)
-        af[im] = *reinterpret_cast<const h8_t*>(la + (wm * 64 + im * 32 + (lane & 31)) * kPitch + 16 * s + 8 * (lane >> 5));
+      for (int im = 0; im < kWM; ++im) af[im] = decode8(wa[im][s], sa[im][s >> 1]);
 #pragma unroll
-      for (int in = 0; in < 4; ++in)
-        bf[in] = *reinterpret_cast<const h8_t*>(lb + (wn * 128 + in * 32 + (lane & 31)) * kPitch + 16 * s + 8 * (lane >> 5));
+      for (int in = 0; in < kWN; ++in) bf[in] = decode8(wb[in][s], sb[in][s >> 1]);
 #pragma unroll
-      for (int im = 0; im < 2; ++im)
+      for (int im = 0; im < kWM; ++im)
 #pragma unroll
-        for (int in = 0; in < 4; ++in)
+        for (int in = 0; in < kWN; ++in)
           acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[im], bf[in], acc[im][in], 0, 0, 0);
     }
     __syncthreads();
@@ -166,23 +217,27 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
 
 // out[i, j] = (acc * sa[i]) * sb[j] for i < rows_i, j < rows_j; the line
 // scales of the tile are staged in LDS first.
-__device__ __forceinline__ void epilogue(const f32x16 (&acc)[2][4], const float* a_amax, uint32_t rows_i,
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[kWM][kWN], const float* a_amax, uint32_t rows_i,
                                          const float* b_amax, uint32_t rows_j, float* out, int64_t ldo,
                                          float* lsa, float* lsb) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (tid < kBM) lsa[tid] = (uint32_t)tid < rows_i ? a_amax[tid] / 2688.0f : 0.0f;
-  lsb[tid] = (uint32_t)tid < rows_j ? b_amax[tid] / 2688.0f : 0.0f;
-  __syncthreads();
-  const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int in = 0; in < 4; ++in) {
-    const uint32_t j = wn * 128 + in * 32 + (lane & 31);
+  for (int c = 0; c < kBN / kThreads; ++c) {
+    const uint32_t j = tid + kThreads * c;
+    lsb[j] = j < rows_j ? b_amax[j] / 2688.0f : 0.0f;
+  }
+  __syncthreads();
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+#pragma unroll
+  for (int in = 0; in < kWN; ++in) {
+    const uint32_t j = wn * (kWN * 32) + in * 32 + (lane & 31);
     const float sb = lsb[j];
 #pragma unroll
-    for (int im = 0; im < 2; ++im)
+    for (int im = 0; im < kWM; ++im)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const uint32_t i = wm * 64 + im * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const uint32_t i = wm * (kWM * 32) + im * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (i < rows_i && j < rows_j) out[(int64_t)i * ldo + j] = (acc[im][in][v] * lsa[i]) * sb;
       }
   }
@@ -190,17 +245,16 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[2][4], const float*
 
 // Forward form: expert e's rows of a times b_e^T.  Tiles: 128-row tiles of
 // the routed rows (each inside one expert) x 256-column tiles of n.
-__global__ __launch_bounds__(kThreads, 2) void gemm_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gemm_fwd_kernel(
     const uint8_t* __restrict__ a_data, const uint8_t* __restrict__ a_scale, const float* __restrict__ a_amax,
     const uint8_t* __restrict__ b_data, const uint8_t* __restrict__ b_scale, const float* __restrict__ b_amax,
     int64_t n, int64_t k, Routing R, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) _Float16 la[kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) _Float16 lb[kBN * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
   __shared__ float lsa[kBM], lsb[kBN];
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
   uint32_t tm, tn;
-  grouped_tile(xcd_logical_id(), ntm, ntn, &tm, &tn);
+  grouped_tile(xcd_supertile_id(), ntm, ntn, &tm, &tn);
   const int32_t row0 = (int32_t)(tm * kBM);
   if (row0 >= total) return;
   int32_t rbeg, rend;
@@ -210,12 +264,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fwd_kernel(
   const int64_t brow0 = (int64_t)e * n + col0;  // first line of b in this tile
   const OperandTile A{a_data + (int64_t)row0 * (k / 2), a_scale + (int64_t)row0 * (k / 16), (uint32_t)kBM};
   const OperandTile B{b_data + brow0 * (k / 2), b_scale + brow0 * (k / 16), cols};
-  f32x16 acc[2][4];
+  f32x16 acc[kWM][kWN];
 #pragma unroll
-  for (int im = 0; im < 2; ++im)
+  for (int im = 0; im < kWM; ++im)
 #pragma unroll
-    for (int in = 0; in < 4; ++in) acc[im][in] = f32x16{};
-  gemm_tile(A, B, (uint32_t)k, acc, la, lb);
+    for (int in = 0; in < kWN; ++in) acc[im][in] = f32x16{};
+  gemm_tile(A, B, (uint32_t)k, acc, lds);
   epilogue(acc, a_amax + row0, kBM, b_amax + brow0, cols, out + (int64_t)row0 * n + col0, n, lsa, lsb);
 }
 
@@ -223,15 +277,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fwd_kernel(
 // xa_e[i, r] * xb_e[j, r], with a and b columnwise cast outputs (expert e's
 // lines at byte n*r_e/2 resp. k*r_e/2, line length M_e).  Tiles: per expert,
 // 128-line tiles of a x 256-line tiles of b.
-__global__ __launch_bounds__(kThreads, 2) void gemm_wgrad_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gemm_wgrad_kernel(
     const uint8_t* __restrict__ a_data, const uint8_t* __restrict__ a_scale, const float* __restrict__ a_amax,
     const uint8_t* __restrict__ b_data, const uint8_t* __restrict__ b_scale, const float* __restrict__ b_amax,
     int64_t n, int64_t k, Routing R, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) _Float16 la[kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) _Float16 lb[kBN * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
   __shared__ float lsa[kBM], lsb[kBN];
   if (!routing_ok(R)) return;
-  const uint32_t t = xcd_logical_id(), per = ntm * ntn;
+  const uint32_t t = xcd_supertile_id(), per = ntm * ntn;
   const int e = (int)uni(t / per);
   uint32_t tm, tn;
   grouped_tile(t % per, ntm, ntn, &tm, &tn);
@@ -243,12 +296,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_wgrad_kernel(
                       rows_i};
   const OperandTile B{b_data + k * (int64_t)rbeg / 2 + j0 * (me / 2), b_scale + k * (int64_t)rbeg / 16 + j0 * (me / 16),
                       rows_j};
-  f32x16 acc[2][4];
+  f32x16 acc[kWM][kWN];
 #pragma unroll
-  for (int im = 0; im < 2; ++im)
+  for (int im = 0; im < kWM; ++im)
 #pragma unroll
-    for (int in = 0; in < 4; ++in) acc[im][in] = f32x16{};
-  gemm_tile(A, B, me, acc, la, lb);
+    for (int in = 0; in < kWN; ++in) acc[im][in] = f32x16{};
+  gemm_tile(A, B, me, acc, lds);
   epilogue(acc, a_amax + (int64_t)e * n + i0, rows_i, b_amax + (int64_t)e * k + j0, rows_j,
            out + (int64_t)e * n * k + i0 * k + j0, k, lsa, lsb);
 }
@@ -256,6 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_wgrad_kernel(
 // ------------------------------------------------------------- host side
 
 constexpr int64_t kGemmMaxN = 1 << 20;
+constexpr int64_t kGemmMaxExpertRows = 1 << 22;  // weight gradient: rows of one expert
 
 int check_gemm_ptrs(const uint8_t* ad, const uint8_t* as, const float* aa, const uint8_t* bd, const uint8_t* bs,
                     const float* ba, const float* out) {
@@ -334,6 +388,9 @@ int nvfp4_group_gemm_wgrad(const uint8_t* a_col_data, const uint8_t* a_col_scale
   R.d_offs = nullptr;
   R.d_status = nullptr;
   if ((rc = host_routing(h_splits, sum_m, num_experts, &R))) return rc;
+  // a work-group's operand lines are addressed with 32-bit byte offsets
+  for (int32_t e = 0; e < num_experts; ++e)
+    if (h_splits[e] > kGemmMaxExpertRows) return NVFP4G_EINVAL;
   hipLaunchKernelGGL(gemm_wgrad_kernel, dim3((uint32_t)(ntm * ntn * num_experts)), dim3(kThreads), 0,
                      (hipStream_t)stream, a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax,
                      n, k, R, (uint32_t)ntm, (uint32_t)ntn, out);

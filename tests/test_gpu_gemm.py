@@ -202,3 +202,18 @@ def test_wgrad_exact_on_exactly_representable_operands():
         assert (want[e] == dY[r0:r0 + m].T @ X[r0:r0 + m]).all()
         r0 += m
     assert (got == want).all(), f"{int((got != want).sum())} inexact outputs"
+
+
+def test_fwd_random_operand_bytes():
+    # every code byte and every finite E4M3 scale code, subnormal scales and
+    # zero scales included, so each decode step is exercised on all inputs
+    rng = np.random.default_rng(91)
+    splits, n, k = [128, 256], 80, 512
+    E, sum_m = len(splits), sum(splits)
+    a = (rng.integers(0, 256, (sum_m, k // 2), dtype=np.uint8), rng.integers(0, 0x7F, (sum_m, k // 16), dtype=np.uint8),
+         rng.uniform(0.5, 2.0, sum_m).astype(np.float32))
+    b = (rng.integers(0, 256, (E * n, k // 2), dtype=np.uint8), rng.integers(0, 0x7F, (E * n, k // 16), dtype=np.uint8),
+         rng.uniform(0.5, 2.0, E * n).astype(np.float32))
+    want, bound = O.group_gemm(*a, b[0].reshape(E, n, -1), b[1].reshape(E, n, -1), b[2], splits, n, k)
+    out = run_fwd(a, b, splits, n, k)
+    check_close(out.numpy(), want, bound, k, "fwd random bytes")
