@@ -15,9 +15,10 @@ vectors written once and read once, and both outputs written once.
 
 On workloads with both directions the JSON line also carries ``next_rows``:
 the grouped MXFP4 cast of the same input (one read of x, both MXFP4 outputs
-written) and the rowwise / columnwise NVFP4 dequant of the step's outputs
-(codes, scales and line amax read once, fp32 written), each timed with HIP
-events over repeated launches.
+written), the rowwise / columnwise NVFP4 dequant of the step's outputs
+(codes, scales and line amax read once, fp32 written), and the row-scaled
+grouped GEMM (forward and weight gradient, MFMA-bound, TFLOP/s against the
+fp16 MFMA peak), each timed with HIP events over repeated launches.
 """
 from __future__ import annotations
 
@@ -286,6 +287,52 @@ def next_rows(B, torch, tev, x, splits, out, E: int, k: int, m: int, reps: int) 
     ms = timed(lambda: B.nvfp4_group_dequant_columnwise(out["col_data"], out["col_scale"], out["col_amax"],
                                                          splits, k, deq))
     res["nvfp4_group_dequant_columnwise"] = entry("dequant_kernel", ms, N // 2 + N // 16 + 4 * E * k + 4 * N)
+    del deq
+    res.update(gemm_rows(B, torch, timed, out, splits, E, k, m))
+    return res
+
+
+GEMM_N = 2048          # a DeepSeek-V3 expert's gate projection: hidden 7168 -> intermediate 2048
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def gemm_rows(B, torch, timed, out, splits, E: int, k: int, m: int) -> dict:
+    """Row-scaled grouped GEMM on the step's outputs: the forward product of
+    the rowwise cast (A) with per-expert NVFP4 weights [E, GEMM_N, k], and the
+    weight gradient of the columnwise cast (B) with a columnwise dY operand.
+    Weight and dY operands are seeded random FP4 codes, finite E4M3 scales
+    and positive amax (the kernels' time does not depend on the values)."""
+    print("[bench] grouped GEMM", file=sys.stderr, flush=True)
+    if k % 128:
+        return {}
+    dev = out["row_data"].device
+    n = GEMM_N
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    codes = lambda *shape: torch.randint(0, 256, shape, dtype=torch.uint8, device=dev, generator=g)
+    scales = lambda *shape: torch.randint(0x20, 0x50, shape, dtype=torch.uint8, device=dev, generator=g)
+    amax = lambda n_: torch.rand(n_, device=dev, generator=g) + 0.5
+    flops = 2.0 * m * n * k
+
+    def entry(kernel, ms):
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"kernel": kernel, "avg_us": round(ms * 1e3, 2), "flops_per_launch": flops,
+                "shape": {"sum_m": m, "n": n, "k": k, "num_experts": E},
+                "TFLOPs": round(tf, 1), "bound": "mfma", "peak_TFLOPs": MFMA_F16_PEAK_TFLOPS,
+                "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+
+    res = {}
+    w = (codes(E, n, k // 2), scales(E, n, k // 16), amax(E * n))
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ms = timed(lambda: B.nvfp4_group_gemm(out["row_data"], out["row_scale"], out["row_amax"], *w, splits, y))
+    res["nvfp4_group_gemm"] = entry("gemm_fwd_kernel", ms)
+    del w, y
+    dy = (codes(m * n // 2), scales(m * n // 16), amax(E * n))
+    dw = torch.empty((E, n, k), dtype=torch.float32, device=dev)
+    ms = timed(lambda: B.nvfp4_group_gemm_wgrad(*dy, out["col_data"], out["col_scale"], out["col_amax"], splits,
+                                                n, k, dw))
+    res["nvfp4_group_gemm_wgrad"] = entry("gemm_wgrad_kernel", ms)
+    del dy, dw
     return res
 
 

@@ -227,7 +227,7 @@ int mxfp4_group_cast_graphsafe(const uint16_t* x, int64_t m_capacity,
  * with acc the fp32 MFMA sum of the exact products value(code)*value(S)
  * (fp16 operands).  For the data gradient pass the columnwise cast of each
  * expert's weight as b.  out: fp32 [sum_m, n], row-major, caller-owned.
- * k a positive multiple of 64 (<= 2^22), n a positive multiple of 16
+ * k a positive multiple of 128 (<= 2^22), n a positive multiple of 16
  * (<= 2^20); data pointers 16-byte aligned, scale and amax pointers 4-byte
  * aligned; otherwise NVFP4G_EINVAL / NVFP4G_EALIGN and nothing is enqueued. */
 int nvfp4_group_gemm(const uint8_t* a_data, const uint8_t* a_scale,

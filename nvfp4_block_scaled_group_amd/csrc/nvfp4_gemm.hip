@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/nvfp4_group.h"
 #include "nvfp4_common.hpp"
 #include "nvfp4_numerics.hpp"
@@ -60,7 +62,8 @@ constexpr int kBM = kWavesM * kWM * 32;  // tile rows (i): 128
 constexpr int kBN = kWavesN * kWN * 32;  // tile columns (j): 512
 static_assert(kBM == 128, "row tiles must be the 128-row expert granule");
 static_assert(kBN % kThreads == 0, "each thread copies whole B lines");
-constexpr int kBK = 64;             // contraction step
+constexpr int kBK = 128;            // contraction step
+constexpr int kStages = 2;          // LDS stages (double buffer)
 constexpr int kGroupRows = 8;       // row tiles per column sweep
 
 // One NT operand tile: `rows` lines of length L starting at the tile's first
@@ -94,10 +97,26 @@ __device__ __forceinline__ void grouped_tile(uint32_t t, uint32_t ntm, uint32_t 
   *tn = uni(in / gm);
 }
 
-// LDS stage: raw FP4 bytes and E4M3 scale bytes of one contraction step,
-// [line][32 bytes] codes and [line][4 bytes] scales for A then B.
-constexpr uint32_t kStA = 0, kStB = kBM * 32, kStAS = kStB + kBN * 32, kStBS = kStAS + kBM * 4;
-constexpr uint32_t kStageBytes = kStBS + kBN * 4;
+// LDS stage: the raw FP4 bytes and E4M3 scale bytes of one contraction step,
+// [line][64 bytes] codes and [line][8 bytes] scales for A, then for B.
+constexpr uint32_t kRowBytes = kBK / 2, kRowScales = kBK / 16;
+constexpr uint32_t kStA = 0, kStB = kBM * kRowBytes, kStAS = kStB + kBN * kRowBytes,
+                   kStBS = kStAS + kBM * kRowScales;
+constexpr uint32_t kStageBytes = kStBS + kBN * kRowScales;  // 46080
+// copies per thread per stage (direct global -> LDS loads): 16-byte code
+// granules of A and B, 4-byte scale words of A and B
+constexpr int kCpA = kBM * kRowBytes / 16 / kThreads, kCpB = kBN * kRowBytes / 16 / kThreads;
+constexpr int kCpAS = kBM * kRowScales / 4 / kThreads, kCpBS = kBN * kRowScales / 4 / kThreads;
+static_assert(kCpA * 16 * kThreads == kBM * kRowBytes && kCpB * 16 * kThreads == kBN * kRowBytes &&
+              kCpAS * 4 * kThreads == kBM * kRowScales && kCpBS * 4 * kThreads == kBN * kRowScales,
+              "every thread issues the same copies");
+constexpr uint32_t kLdsBytes = kStages * kStageBytes;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt that waits until at most n vector-memory operations of this wave
+// are outstanding (and nothing else).
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Two E4M3 codes (low byte first) -> their fp16 values (exact: the fp8
 // convert with unit scale).
@@ -116,16 +135,24 @@ __device__ __forceinline__ h8_t decode8(uint32_t w, _Float16 S) {
   return h8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// acc[im][in] += A[64 lines of the wave] x B[128 lines of the wave]^T over
-// the contraction length L (a multiple of kBK).
+// acc[im][in] += A[lines of the wave] x B[lines of the wave]^T over the
+// contraction length L (a multiple of kBK).
 //
-// Contraction order: the MFMA's 16 k-slots of sub-step s are, for lanes
-// 0-31 (h = 0) and 32-63 (h = 1), the 8 elements of byte word 4h + s of the
-// line's 32-byte step chunk.  A and B use the same assignment, so the sum is
-// the same; it lets each lane fetch its words of all four sub-steps with one
-// 16-byte LDS read, and its two block scales (blocks 2h, 2h+1) with one
-// 2-byte read.  LDS holds raw FP4 (double-buffered); each wave decodes its
-// own fragments right before the MFMAs.
+// Contraction order: the MFMA's 16 k-slots of sub-step s (0..7) are, for
+// lanes 0-31 (h = 0) and 32-63 (h = 1), the 8 elements of 4-byte word
+// 8h + s of the line's 64-byte step chunk.  A and B use the same
+// assignment, so the sum is unchanged; each lane reads its words of all
+// eight sub-steps with two 16-byte LDS reads and the four block scales it
+// needs (blocks 4h .. 4h+3) with one 4-byte read.
+//
+// Pipeline (double-buffered LDS): each step starts with the wave waiting
+// for its own copies of the step (issued one step earlier) and a work-group
+// barrier, so the step is complete in LDS and the other stage is no longer
+// being read; every wave then reads all its fragments of the step into
+// registers, issues the direct global -> LDS copies of the next step into the
+// other stage, and multiplies while those copies are in flight.  (LDS reads
+// must come before the next copies are issued: the compiler makes an LDS
+// read wait for every copy in flight.)
 __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTile& B, uint32_t L,
                                           f32x16 (&acc)[kWM][kWN], uint8_t* lds) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -138,81 +165,87 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
   };
   const rsrc_t ad = rsrc(A.data, av * dpitch), as = rsrc(A.scale, av * spitch);
   const rsrc_t bd = rsrc(B.data, bv * dpitch), bs = rsrc(B.scale, bv * spitch);
-  // copy roles: A codes 16 bytes (line tid/2, half tid&1), A scales 4 bytes
-  // (line tid, threads < 128), B codes 32 bytes and B scales 4 bytes (line tid)
-  const uint32_t a_doff = (uint32_t)(tid >> 1) * dpitch + 16u * (tid & 1);
-  const uint32_t a_soff = tid < kBM ? (uint32_t)tid * spitch : kOutOfRange;
-  constexpr int kBL = kBN / kThreads;  // B lines copied per thread: tid + kThreads * c
-  u32x4 ra, rb[kBL][2];
-  uint32_t ras = 0, rbs[kBL];
-  auto load = [&](uint32_t ks) {
-    ra = __builtin_amdgcn_raw_buffer_load_b128(ad, a_doff, ks * 32u, 0);
-    if (tid < kBM) ras = __builtin_amdgcn_raw_buffer_load_b32(as, a_soff, ks * 4u, 0);
-#pragma unroll
-    for (int c = 0; c < kBL; ++c) {
-      const uint32_t line = (uint32_t)(tid + kThreads * c);
-      rb[c][0] = __builtin_amdgcn_raw_buffer_load_b128(bd, line * dpitch, ks * 32u, 0);
-      rb[c][1] = __builtin_amdgcn_raw_buffer_load_b128(bd, line * dpitch + 16u, ks * 32u, 0);
-      rbs[c] = __builtin_amdgcn_raw_buffer_load_b32(bs, line * spitch, ks * 4u, 0);
-    }
-  };
-  auto store = [&](uint32_t st) {
+  const uint32_t nk = L / kBK;
+  if (nk == 0) return;
+
+  // Copy step ks into stage st.  Copy c of a thread moves granule
+  // g = c * kThreads + tid; a wave's lanes land contiguously in LDS.
+  auto issue = [&](uint32_t ks, uint32_t st) {
     uint8_t* base = lds + st * kStageBytes;
-    *reinterpret_cast<u32x4*>(base + kStA + 16 * tid) = ra;
-    if (tid < kBM) *reinterpret_cast<uint32_t*>(base + kStAS + 4 * tid) = ras;
+    const uint32_t sd = ks * kRowBytes, ss = ks * kRowScales;
 #pragma unroll
-    for (int c = 0; c < kBL; ++c) {
-      const int line = tid + kThreads * c;
-      *reinterpret_cast<u32x4*>(base + kStB + 32 * line) = rb[c][0];
-      *reinterpret_cast<u32x4*>(base + kStB + 32 * line + 16) = rb[c][1];
-      *reinterpret_cast<uint32_t*>(base + kStBS + 4 * line) = rbs[c];
+    for (int c = 0; c < kCpA; ++c) {
+      const uint32_t g = c * kThreads + tid;  // line g / 4, quarter g % 4
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ad, (lds_ptr_t)(base + kStA + 16 * (c * kThreads + wave * 64)), 16,
+                                               (g >> 2) * dpitch + 16 * (g & 3), sd, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kCpB; ++c) {
+      const uint32_t g = c * kThreads + tid;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bd, (lds_ptr_t)(base + kStB + 16 * (c * kThreads + wave * 64)), 16,
+                                               (g >> 2) * dpitch + 16 * (g & 3), sd, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kCpAS; ++c) {
+      const uint32_t g = c * kThreads + tid;  // line g / 2, half g % 2
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(as, (lds_ptr_t)(base + kStAS + 4 * (c * kThreads + wave * 64)), 4,
+                                               (g >> 1) * spitch + 4 * (g & 1), ss, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kCpBS; ++c) {
+      const uint32_t g = c * kThreads + tid;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs, (lds_ptr_t)(base + kStBS + 4 * (c * kThreads + wave * 64)), 4,
+                                               (g >> 1) * spitch + 4 * (g & 1), ss, 0, 0);
     }
   };
 
   const int wm = wave / kWavesN, wn = wave % kWavesN, h = lane >> 5;
-  const uint32_t nk = L / kBK;
-  if (nk == 0) return;
-  load(0);
-  store(0);
-  if (nk > 1) load(1);
-  __syncthreads();
+  issue(0, 0);
 #pragma unroll 1
   for (uint32_t ks = 0; ks < nk; ++ks) {
-    const uint32_t cur = ks & 1;
-    if (ks + 1 < nk) {
-      store(cur ^ 1);
-      if (ks + 2 < nk) load(ks + 2);
-    }
-    const uint8_t* base = lds + cur * kStageBytes;
-    u32x4 wa[kWM], wb[kWN];
-    h2_t sa[kWM], sb[kWN];
+    const uint32_t st = ks & 1;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of step ks
+    __syncthreads();
+    const uint8_t* base = lds + st * kStageBytes;
+    u32x4 wa[kWM][2], wb[kWN][2];
+    h2_t sa[kWM][2], sb[kWN][2];
 #pragma unroll
     for (int im = 0; im < kWM; ++im) {
       const uint32_t line = wm * (kWM * 32) + im * 32 + (lane & 31);
-      wa[im] = *reinterpret_cast<const u32x4*>(base + kStA + 32 * line + 16 * h);
-      sa[im] = scales_h2(*reinterpret_cast<const uint16_t*>(base + kStAS + 4 * line + 2 * h));
+      wa[im][0] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 32 * h);
+      wa[im][1] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 32 * h + 16);
+      const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + kStAS + kRowScales * line + 4 * h);
+      sa[im][0] = scales_h2(sc & 0xFFFFu);
+      sa[im][1] = scales_h2(sc >> 16);
     }
 #pragma unroll
     for (int in = 0; in < kWN; ++in) {
       const uint32_t line = wn * (kWN * 32) + in * 32 + (lane & 31);
-      wb[in] = *reinterpret_cast<const u32x4*>(base + kStB + 32 * line + 16 * h);
-      sb[in] = scales_h2(*reinterpret_cast<const uint16_t*>(base + kStBS + 4 * line + 2 * h));
+      wb[in][0] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 32 * h);
+      wb[in][1] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 32 * h + 16);
+      const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + kStBS + kRowScales * line + 4 * h);
+      sb[in][0] = scales_h2(sc & 0xFFFFu);
+      sb[in][1] = scales_h2(sc >> 16);
     }
+    if (ks + 1 < nk) issue(ks + 1, st ^ 1);
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
       h8_t af[kWM], bf[kWN];
+      // sub-step s: word s of the lane's 8, block s / 2 of its 4
 #pragma unroll
-      for (int im = 0; im < kWM; ++im) af[im] = decode8(wa[im][s], sa[im][s >> 1]);
+      for (int im = 0; im < kWM; ++im) af[im] = decode8(wa[im][s >> 2][s & 3], sa[im][s >> 2][(s >> 1) & 1]);
 #pragma unroll
-      for (int in = 0; in < kWN; ++in) bf[in] = decode8(wb[in][s], sb[in][s >> 1]);
+      for (int in = 0; in < kWN; ++in) bf[in] = decode8(wb[in][s >> 2][s & 3], sb[in][s >> 2][(s >> 1) & 1]);
 #pragma unroll
       for (int im = 0; im < kWM; ++im)
 #pragma unroll
         for (int in = 0; in < kWN; ++in)
           acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[im], bf[in], acc[im][in], 0, 0, 0);
     }
-    __syncthreads();
   }
+  // the stages are reused by the epilogue's staging only after every wave is done
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
 }
 
 // out[i, j] = (acc * sa[i]) * sb[j] for i < rows_i, j < rows_j; the line
@@ -249,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fwd_kernel(
     const uint8_t* __restrict__ a_data, const uint8_t* __restrict__ a_scale, const float* __restrict__ a_amax,
     const uint8_t* __restrict__ b_data, const uint8_t* __restrict__ b_scale, const float* __restrict__ b_amax,
     int64_t n, int64_t k, Routing R, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   __shared__ float lsa[kBM], lsb[kBN];
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
@@ -273,6 +306,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fwd_kernel(
   epilogue(acc, a_amax + row0, kBM, b_amax + brow0, cols, out + (int64_t)row0 * n + col0, n, lsa, lsb);
 }
 
+// Expert order of the weight-gradient tiles: the experts with the most rows
+// (the longest contractions) first, so the long tiles do not form the tail.
+struct ExpertOrder {
+  uint16_t e[NVFP4G_MAX_EXPERTS_HOST];
+};
+
 // Weight-gradient form: for expert e, out_e[i, j] = sum over its rows r of
 // xa_e[i, r] * xb_e[j, r], with a and b columnwise cast outputs (expert e's
 // lines at byte n*r_e/2 resp. k*r_e/2, line length M_e).  Tiles: per expert,
@@ -280,12 +319,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fwd_kernel(
 __global__ __launch_bounds__(kThreads, 1) void gemm_wgrad_kernel(
     const uint8_t* __restrict__ a_data, const uint8_t* __restrict__ a_scale, const float* __restrict__ a_amax,
     const uint8_t* __restrict__ b_data, const uint8_t* __restrict__ b_scale, const float* __restrict__ b_amax,
-    int64_t n, int64_t k, Routing R, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+    int64_t n, int64_t k, Routing R, ExpertOrder order, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   __shared__ float lsa[kBM], lsb[kBN];
   if (!routing_ok(R)) return;
   const uint32_t t = xcd_supertile_id(), per = ntm * ntn;
-  const int e = (int)uni(t / per);
+  const int e = (int)uni((uint32_t)order.e[t / per]);
   uint32_t tm, tn;
   grouped_tile(t % per, ntm, ntn, &tm, &tn);
   const int32_t rend = route_end(R, e), rbeg = e ? route_end(R, e - 1) : 0;
@@ -391,9 +430,13 @@ int nvfp4_group_gemm_wgrad(const uint8_t* a_col_data, const uint8_t* a_col_scale
   // a work-group's operand lines are addressed with 32-bit byte offsets
   for (int32_t e = 0; e < num_experts; ++e)
     if (h_splits[e] > kGemmMaxExpertRows) return NVFP4G_EINVAL;
+  ExpertOrder order;
+  for (int32_t e = 0; e < num_experts; ++e) order.e[e] = (uint16_t)e;
+  std::stable_sort(order.e, order.e + num_experts,
+                   [&](uint16_t a, uint16_t b) { return h_splits[a] > h_splits[b]; });
   hipLaunchKernelGGL(gemm_wgrad_kernel, dim3((uint32_t)(ntm * ntn * num_experts)), dim3(kThreads), 0,
                      (hipStream_t)stream, a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax,
-                     n, k, R, (uint32_t)ntm, (uint32_t)ntn, out);
+                     n, k, R, order, (uint32_t)ntm, (uint32_t)ntn, out);
   return hip_status();
 }
 

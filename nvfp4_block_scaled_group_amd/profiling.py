@@ -36,6 +36,8 @@ KERNEL_SOURCES = {
     "amax_init_kernel": "nvfp4_group.hip",
     "group_quantize_rowwise_kernel": "nvfp4_group.hip",
     "dequant_kernel": "nvfp4_dequant.hip",
+    "gemm_fwd_kernel": "nvfp4_gemm.hip",
+    "gemm_wgrad_kernel": "nvfp4_gemm.hip",
 }
 KERNELS = tuple(KERNEL_SOURCES)
 

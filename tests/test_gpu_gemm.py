@@ -89,7 +89,7 @@ def _weights(rng, E, n, k, dist="normal"):
 @pytest.mark.parametrize("splits,n,k,dist,seed", [
     ([128, 256, 0, 128], 272, 256, "rowscale", 81),     # ragged n (one partial column tile), empty expert
     ([384, 128], 48, 128, "outliers", 82),              # n below one column tile
-    ([128] * 6, 512, 64, "normal", 83),                 # a single contraction step
+    ([128] * 6, 512, 128, "normal", 83),                # a single contraction step
     ([1024, 0, 512, 2560], 320, 2048, "rowscale", 84),  # several row-tile groups, long contraction
 ])
 def test_fwd_matches_oracle(splits, n, k, dist, seed):
@@ -115,7 +115,7 @@ def _exact_operand(rng, rows, k):
 
 def test_fwd_exact_on_exactly_representable_operands():
     rng = np.random.default_rng(85)
-    splits, n, k = [256, 128, 0, 384], 288, 320
+    splits, n, k = [256, 128, 0, 384], 288, 384
     E = len(splits)
     X = _exact_operand(rng, sum(splits), k)
     W = _exact_operand(rng, E * n, k)
@@ -137,7 +137,7 @@ def _weights_from(W):
 
 def test_fwd_graphsafe_equals_host_split_and_skips_unrouted_rows():
     rng = np.random.default_rng(86)
-    splits, n, k = [256, 0, 128], 96, 192
+    splits, n, k = [256, 0, 128], 96, 256
     w = synth.random_case(86, splits, k, "normal")
     a = oracle_rowwise(w.x)
     b = _weights(rng, len(splits), n, k)

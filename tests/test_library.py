@@ -160,7 +160,7 @@ def test_gemm_host_checks(lib):
                                                                    ctypes.c_void_p, ctypes.c_void_p]
     sp = (ctypes.c_int64 * 2)(128, 128)
     ok = [FAKE] * 6
-    assert f(*ok, 256, 32, 96, 2, sp, FAKE, None) == -1            # k not a multiple of 64
+    assert f(*ok, 256, 32, 96, 2, sp, FAKE, None) == -1            # k not a multiple of 128
     assert f(*ok, 256, 24, 128, 2, sp, FAKE, None) == -1           # n not a multiple of 16
     assert f(*ok, 256, 0, 128, 2, sp, FAKE, None) == -1            # n = 0
     assert f(*ok, 256, 32, 128, 2, sp, None, None) == -1           # no output
