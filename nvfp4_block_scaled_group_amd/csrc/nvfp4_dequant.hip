@@ -24,15 +24,18 @@ namespace {
 
 using namespace nvfp4g;
 
-// Work unit: a chunk of 1024 consecutive output elements per wave.  Lane l
-// decodes the four elements 256g + 4l .. +3 of the chunk for g = 0..3, so
-// each of the wave's four 16-byte stores covers 1 KB of contiguous output.
+// Work unit: a chunk of 2048 consecutive output elements per wave.  Lane l
+// decodes the four elements 256g + 4l .. +3 of the chunk for g = 0..7, so
+// each of the wave's eight 16-byte stores covers 1 KB of contiguous output.
 // A 16-element block (and so a line) never splits across a lane's group of
 // four.  In the columnwise layout expert e's span [K*r_e, K*r_{e+1}) is a
 // multiple of 2048 elements (r_e a multiple of 128, K of 16), so a chunk
-// lies in one expert: the expert search and the 64-bit division that
-// places the chunk on its first line are per chunk and wave-uniform.
-constexpr int kChunk = 1024;
+// lies in one expert: the expert search and the 64-bit division that places
+// the chunk on its first line are per chunk and wave-uniform.  All loads of
+// a chunk (codes, scale bytes, line amax) are issued before any is used, so
+// a chunk costs one memory round trip.
+constexpr int kChunk = 2048;
+constexpr int kGroups = kChunk / 256;
 
 // Magnitudes of the E2M1 codes 0..7 in units of 0.5 (0 1 2 3 4 6 8 12),
 // one nibble each.
@@ -43,7 +46,9 @@ constexpr uint32_t kE2m1Halves = 0xC8643210u;
 // 4-bit integer times an E4M3 value), so the one rounding is the product
 // with s, as in (value(code) * value(S)) * s; the sign is applied last
 // (rounding to nearest is symmetric).
-__device__ __forceinline__ float4 decode4(uint32_t q, float hS, float s) {
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 decode4(uint32_t q, float hS, float s) {
   float r[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -51,7 +56,7 @@ __device__ __forceinline__ float4 decode4(uint32_t q, float hS, float s) {
     const float mag = (float)((kE2m1Halves >> ((c & 7u) * 4u)) & 15u) * hS;
     r[j] = __uint_as_float(__float_as_uint(mag * s) | ((c & 8u) << 28));
   }
-  return make_float4(r[0], r[1], r[2], r[3]);
+  return f32x4{r[0], r[1], r[2], r[3]};
 }
 
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
@@ -86,20 +91,29 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t* sch = scale + c0 / 16;
     const float* ach = amax + uni(lbase);
     float* och = out + c0;
+    uint32_t q[kGroups], sb[kGroups];
+    float A[kGroups];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < kGroups; ++g) {
       const uint32_t o = 256u * g + 4u * lane;
-      if (o >= left) break;
+      const bool live = o < left;
       // line offset (urem + o) / ulen: float estimate, then one correction
       // step (the estimate is within 1 for quotients below 2^22)
       const uint32_t v = urem + o;
       uint32_t d = (uint32_t)((float)v * inv_len);
       const int32_t rem = (int32_t)(v - d * ulen);
       d = rem < 0 ? d - 1 : (rem >= (int32_t)ulen ? d + 1 : d);
-      const float s = ach[d] / 2688.0f;
-      const float hS = e4m3_value(sch[o / 16]) * 0.5f;
-      const uint32_t q = *reinterpret_cast<const uint16_t*>(dch + o / 2);
-      *reinterpret_cast<float4*>(och + o) = decode4(q, hS, s);
+      q[g] = live ? *reinterpret_cast<const uint16_t*>(dch + o / 2) : 0u;
+      sb[g] = live ? sch[o / 16] : 0u;
+      A[g] = live ? ach[d] : 0.0f;
+    }
+    // streaming (non-temporal) stores: the fp32 output is written once and
+    // is far larger than the caches
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const uint32_t o = 256u * g + 4u * lane;
+      if (o < left) __builtin_nontemporal_store(decode4(q[g], e4m3_value(sb[g]) * 0.5f, A[g] / 2688.0f),
+                                                reinterpret_cast<f32x4*>(och + o));
     }
   }
 }
@@ -108,7 +122,7 @@ int launch_dequant(const uint8_t* data, const uint8_t* scale, const float* amax,
                    bool columnwise, const Routing& R, float* out, hipStream_t st) {
   if (n_elems == 0) return NVFP4G_OK;
   const int64_t waves = (n_elems + kChunk - 1) / kChunk;
-  const unsigned grid = (unsigned)std::min<int64_t>((waves + 3) / 4, 4096);
+  const unsigned grid = (unsigned)std::min<int64_t>((waves + 3) / 4, 8192);
   hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kThreads), 0, st, data, scale, amax, k, n_elems, columnwise,
                      R, out);
   return hip_status();
