@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void mxfp4_group_cast_kernel(
       hi = FP4X2(hi, XCOL(12), XCOL(13), 2);
       hi = FP4X2(hi, XCOL(14), XCOL(15), 3);
 #undef XCOL
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, cd, vo, (uint32_t)j * (me / 2), kStoreAux);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, cd, vo, (uint32_t)j * (me / 2), kStoreStream);
       if ((j >> 2) == (rb & 1))  // the lane pair splits the 8 columns' scale writes
         reinterpret_cast<uint8_t*>(&l_cs[lcol + j])[rb >> 1] = (uint8_t)byte;
     }

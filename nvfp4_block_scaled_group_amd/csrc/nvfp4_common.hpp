@@ -103,6 +103,12 @@ constexpr int kLoadStream = 2;
 #define NVFP4G_STORE_AUX 0
 #endif
 constexpr int kStoreAux = NVFP4G_STORE_AUX;
+// Streaming (non-temporal) stores, for the transposed (columnwise) data: its
+// two 64-byte halves of a 128-byte line come from vertically adjacent tiles
+// processed together on one XCD, and writing them past the caches' normal
+// retention measured faster than plain stores (plain stores stay better for
+// the rowwise data and for the small scale stores).
+constexpr int kStoreStream = 2;
 
 // ------------------------------------------------------------- tiles
 

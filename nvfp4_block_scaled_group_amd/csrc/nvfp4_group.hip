@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
         hi = FP4X2(hi, XCOL(12), XCOL(13), 2);
         hi = FP4X2(hi, XCOL(14), XCOL(15), 3);
 #undef XCOL
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, cd, vo, (uint32_t)j * (me / 2), kStoreAux);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, cd, vo, (uint32_t)j * (me / 2), kStoreStream);
       }
     }
 
