@@ -2,6 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+Timing: untimed steps for --settle-ms (the clocks of a fresh GPU ramp up
+under load), then --warmup untimed steps, then exactly --steps timed steps
+between two device synchronisations; per-kernel times come from HIP events
+recorded on the launch stream.
+
 A step is one pass of the whole path over the workload: the grouped amax
 (rowwise + per-expert columnwise) then the grouped cast (rowwise +
 transposed), through the C ABI, with the input resident in HBM.  The default
@@ -127,8 +132,11 @@ def cpu_baseline(w, target_rows: int = 6144) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="untimed steps for this long before the warmup steps: the GPU's clocks ramp up over "
+                         "the first tens of milliseconds of load on a fresh box (0: skip)")
     ap.add_argument("--workload", default="deepseek_share",
                     choices=["deepseek_share", "down_proj", "outliers", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -179,7 +187,11 @@ def main():
         if ev is not None:
             tev.record(ev[2])
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] settle {args.settle_ms:.0f} ms, warmup {args.warmup}", file=sys.stderr, flush=True)
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
