@@ -25,13 +25,14 @@
 // besides the three fp32 operations of the epilogue.
 //
 // Design:
-//  * Work-group tile 128 (i) x 512 (j); 4 wave64s side by side along j, each
-//    computing 128 x 128 with 4 x 4 v_mfma_f32_32x32x16_f16 (256 fp32
-//    accumulators per lane, held in AGPRs); the contraction advances 64
+//  * Work-group tile 128 (i) x 256 (j); 4 wave64s in a 2 x 2 grid, each
+//    computing 64 x 128 with 2 x 4 v_mfma_f32_32x32x16_f16 (128 fp32
+//    accumulators per lane), two work-groups per CU so one's barrier and
+//    LDS phase overlaps the other's MFMAs; the contraction advances 128
 //    elements per step.
 //  * LDS holds the raw step: FP4 bytes and E4M3 scale bytes of the A and B
-//    lines (double-buffered; the next step is loaded into registers while
-//    the current one is multiplied).  Each wave decodes its own fragments
+//    lines (double-buffered; the next step is copied by direct global -> LDS
+//    loads while the current one is multiplied).  Each wave decodes its own fragments
 //    right before the MFMAs: v_cvt_scalef32_pk_f16_fp4 with unit scale gives
 //    the exact E2M1 values two at a time, one packed fp16 multiply applies
 //    value(S) (converted once per block pair by v_cvt_scalef32_pk_f16_fp8).
@@ -56,10 +57,10 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kWavesM = 1, kWavesN = 4;  // wave grid of a work-group
-constexpr int kWM = 4, kWN = 4;          // 32 x 32 MFMA tiles per wave (i, j)
+constexpr int kWavesM = 2, kWavesN = 2;  // wave grid of a work-group
+constexpr int kWM = 2, kWN = 4;          // 32 x 32 MFMA tiles per wave (i, j)
 constexpr int kBM = kWavesM * kWM * 32;  // tile rows (i): 128
-constexpr int kBN = kWavesN * kWN * 32;  // tile columns (j): 512
+constexpr int kBN = kWavesN * kWN * 32;  // tile columns (j): 256
 static_assert(kBM == 128, "row tiles must be the 128-row expert granule");
 static_assert(kBN % kThreads == 0, "each thread copies whole B lines");
 constexpr int kBK = 128;            // contraction step
@@ -113,6 +114,14 @@ static_assert(kCpA * 16 * kThreads == kBM * kRowBytes && kCpB * 16 * kThreads ==
 constexpr uint32_t kLdsBytes = kStages * kStageBytes;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS slot of 16-byte granule q (0..3) of a line's 64-byte step chunk.  A
+// fragment read has lanes 0-31 on 32 consecutive lines at the same granule;
+// XOR-ing the granule with bits 2-3 of the line spreads lines r, r+4, r+8,
+// r+12 over different banks (an involution: the copy fetches granule
+// swz(line, slot) into each slot, the reader finds granule q at slot
+// swz(line, q)).
+__device__ __forceinline__ uint32_t swz(uint32_t line, uint32_t q) { return q ^ ((line >> 2) & 3u); }
 
 // s_waitcnt that waits until at most n vector-memory operations of this wave
 // are outstanding (and nothing else).
@@ -175,15 +184,15 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
     const uint32_t sd = ks * kRowBytes, ss = ks * kRowScales;
 #pragma unroll
     for (int c = 0; c < kCpA; ++c) {
-      const uint32_t g = c * kThreads + tid;  // line g / 4, quarter g % 4
+      const uint32_t g = c * kThreads + tid;  // LDS slot g % 4 of line g / 4
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ad, (lds_ptr_t)(base + kStA + 16 * (c * kThreads + wave * 64)), 16,
-                                               (g >> 2) * dpitch + 16 * (g & 3), sd, 0, 0);
+                                               (g >> 2) * dpitch + 16 * swz(g >> 2, g & 3), sd, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < kCpB; ++c) {
       const uint32_t g = c * kThreads + tid;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bd, (lds_ptr_t)(base + kStB + 16 * (c * kThreads + wave * 64)), 16,
-                                               (g >> 2) * dpitch + 16 * (g & 3), sd, 0, 0);
+                                               (g >> 2) * dpitch + 16 * swz(g >> 2, g & 3), sd, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < kCpAS; ++c) {
@@ -212,8 +221,8 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
 #pragma unroll
     for (int im = 0; im < kWM; ++im) {
       const uint32_t line = wm * (kWM * 32) + im * 32 + (lane & 31);
-      wa[im][0] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 32 * h);
-      wa[im][1] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 32 * h + 16);
+      wa[im][0] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 16 * swz(line, 2 * h));
+      wa[im][1] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 16 * swz(line, 2 * h + 1));
       const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + kStAS + kRowScales * line + 4 * h);
       sa[im][0] = scales_h2(sc & 0xFFFFu);
       sa[im][1] = scales_h2(sc >> 16);
@@ -221,8 +230,8 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
 #pragma unroll
     for (int in = 0; in < kWN; ++in) {
       const uint32_t line = wn * (kWN * 32) + in * 32 + (lane & 31);
-      wb[in][0] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 32 * h);
-      wb[in][1] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 32 * h + 16);
+      wb[in][0] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 16 * swz(line, 2 * h));
+      wb[in][1] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 16 * swz(line, 2 * h + 1));
       const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + kStBS + kRowScales * line + 4 * h);
       sb[in][0] = scales_h2(sc & 0xFFFFu);
       sb[in][1] = scales_h2(sc >> 16);
@@ -278,7 +287,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[kWM][kWN], const fl
 
 // Forward form: expert e's rows of a times b_e^T.  Tiles: 128-row tiles of
 // the routed rows (each inside one expert) x 256-column tiles of n.
-__global__ __launch_bounds__(kThreads, 1) void gemm_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 2) void gemm_fwd_kernel(
     const uint8_t* __restrict__ a_data, const uint8_t* __restrict__ a_scale, const float* __restrict__ a_amax,
     const uint8_t* __restrict__ b_data, const uint8_t* __restrict__ b_scale, const float* __restrict__ b_amax,
     int64_t n, int64_t k, Routing R, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
@@ -316,7 +325,7 @@ struct ExpertOrder {
 // xa_e[i, r] * xb_e[j, r], with a and b columnwise cast outputs (expert e's
 // lines at byte n*r_e/2 resp. k*r_e/2, line length M_e).  Tiles: per expert,
 // 128-line tiles of a x 256-line tiles of b.
-__global__ __launch_bounds__(kThreads, 1) void gemm_wgrad_kernel(
+__global__ __launch_bounds__(kThreads, 2) void gemm_wgrad_kernel(
     const uint8_t* __restrict__ a_data, const uint8_t* __restrict__ a_scale, const float* __restrict__ a_amax,
     const uint8_t* __restrict__ b_data, const uint8_t* __restrict__ b_scale, const float* __restrict__ b_amax,
     int64_t n, int64_t k, Routing R, ExpertOrder order, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
