@@ -265,6 +265,21 @@ int nvfp4_group_gemm_wgrad(const uint8_t* a_col_data, const uint8_t* a_col_scale
                            int32_t num_experts, const int64_t* h_splits,
                            float* out, void* stream);
 
+/* Graph-safe weight-gradient form: the routing comes from the device
+ * inclusive row ends d_offs[E] (as in nvfp4_group_cast_graphsafe); the
+ * columnwise operands are laid out for that routing and out [E, n, k] is
+ * fully written (zeros for experts without rows).  m_capacity <= 2^22.  Bad
+ * routing sets NVFP4G_DEV_* bits in *d_status and writes nothing. */
+int nvfp4_group_gemm_wgrad_graphsafe(const uint8_t* a_col_data,
+                                     const uint8_t* a_col_scale,
+                                     const float* a_col_amax,
+                                     const uint8_t* b_col_data,
+                                     const uint8_t* b_col_scale,
+                                     const float* b_col_amax, int64_t m_capacity,
+                                     int64_t n, int64_t k, int32_t num_experts,
+                                     const int32_t* d_offs, float* out,
+                                     int32_t* d_status, void* stream);
+
 /* Static description of a status code. */
 const char* nvfp4_group_strerror(int status);
 

@@ -35,7 +35,7 @@ EXPORTS = (
     "nvfp4_group_cast_graphsafe", "nvfp4_group_quantize", "nvfp4_group_quantize_graphsafe",
     "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
     "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
-    "nvfp4_group_gemm", "nvfp4_group_gemm_graphsafe", "nvfp4_group_gemm_wgrad",
+    "nvfp4_group_gemm", "nvfp4_group_gemm_graphsafe", "nvfp4_group_gemm_wgrad", "nvfp4_group_gemm_wgrad_graphsafe",
     "nvfp4_group_strerror",
 )
 
@@ -73,6 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.nvfp4_group_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P]
     L.nvfp4_group_gemm_graphsafe.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P]
     L.nvfp4_group_gemm_wgrad.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P]
+    L.nvfp4_group_gemm_wgrad_graphsafe.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = ctypes.c_int
     L.nvfp4_group_strerror.argtypes = [ctypes.c_int]
@@ -239,6 +240,14 @@ def nvfp4_group_gemm_wgrad(a_col_data, a_col_scale, a_col_amax, b_col_data, b_co
     _check("nvfp4_group_gemm_wgrad", load_library().nvfp4_group_gemm_wgrad(
         _ptr(a_col_data), _ptr(a_col_scale), _ptr(a_col_amax), _ptr(b_col_data), _ptr(b_col_scale),
         _ptr(b_col_amax), sum_m, int(n), int(k), e, sp, _ptr(out), _stream(stream)))
+
+
+def nvfp4_group_gemm_wgrad_graphsafe(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax,
+                                     m_capacity, num_experts, d_offs, n, k, out, d_status, stream=None):
+    _check("nvfp4_group_gemm_wgrad_graphsafe", load_library().nvfp4_group_gemm_wgrad_graphsafe(
+        _ptr(a_col_data), _ptr(a_col_scale), _ptr(a_col_amax), _ptr(b_col_data), _ptr(b_col_scale),
+        _ptr(b_col_amax), int(m_capacity), int(n), int(k), int(num_experts), _ptr(d_offs), _ptr(out),
+        _ptr(d_status), _stream(stream)))
 
 
 # ---------------------------------------------------------------- helpers

@@ -328,12 +328,13 @@ struct ExpertOrder {
 __global__ __launch_bounds__(kThreads, 2) void gemm_wgrad_kernel(
     const uint8_t* __restrict__ a_data, const uint8_t* __restrict__ a_scale, const float* __restrict__ a_amax,
     const uint8_t* __restrict__ b_data, const uint8_t* __restrict__ b_scale, const float* __restrict__ b_amax,
-    int64_t n, int64_t k, Routing R, ExpertOrder order, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
+    int64_t n, int64_t k, Routing R, ExpertOrder order, bool ordered, uint32_t ntm, uint32_t ntn,
+    float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   __shared__ float lsa[kBM], lsb[kBN];
   if (!routing_ok(R)) return;
   const uint32_t t = xcd_supertile_id(), per = ntm * ntn;
-  const int e = (int)uni((uint32_t)order.e[t / per]);
+  const int e = (int)uni(ordered ? (uint32_t)order.e[t / per] : t / per);
   uint32_t tm, tn;
   grouped_tile(t % per, ntm, ntn, &tm, &tn);
   const int32_t rend = route_end(R, e), rbeg = e ? route_end(R, e - 1) : 0;
@@ -386,6 +387,23 @@ int check_fwd(int64_t rows, int64_t n, int64_t k, int32_t E) {
   return NVFP4G_OK;
 }
 
+int check_wgrad(int64_t rows, int64_t n, int64_t k, int32_t E) {
+  if (n <= 0 || n % 16 != 0 || n > kGemmMaxN || k <= 0 || k % 16 != 0 || k > kGemmMaxN) return NVFP4G_EINVAL;
+  if (rows < 0 || rows > kMaxRows || E < 1) return NVFP4G_EINVAL;
+  const int64_t tiles = ((n + kBM - 1) / kBM) * ((k + kBN - 1) / kBN);
+  if (tiles * E > (int64_t)INT32_MAX) return NVFP4G_EINVAL;
+  return NVFP4G_OK;
+}
+
+int launch_wgrad(const uint8_t* ad, const uint8_t* as, const float* aa, const uint8_t* bd, const uint8_t* bs,
+                 const float* ba, int64_t n, int64_t k, const Routing& R, const ExpertOrder& order, bool ordered,
+                 float* out, hipStream_t st) {
+  const uint32_t ntm = (uint32_t)((n + kBM - 1) / kBM), ntn = (uint32_t)((k + kBN - 1) / kBN);
+  hipLaunchKernelGGL(gemm_wgrad_kernel, dim3(ntm * ntn * (uint32_t)R.num_experts), dim3(kThreads), 0, st, ad, as,
+                     aa, bd, bs, ba, n, k, R, order, ordered, ntm, ntn, out);
+  return hip_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,12 +442,9 @@ int nvfp4_group_gemm_wgrad(const uint8_t* a_col_data, const uint8_t* a_col_scale
                            const uint8_t* b_col_data, const uint8_t* b_col_scale, const float* b_col_amax,
                            int64_t sum_m, int64_t n, int64_t k, int32_t num_experts, const int64_t* h_splits,
                            float* out, void* stream) {
-  if (n <= 0 || n % 16 != 0 || n > kGemmMaxN || k <= 0 || k % 16 != 0 || k > kGemmMaxN) return NVFP4G_EINVAL;
-  if (sum_m < 0 || sum_m > kMaxRows || num_experts < 1) return NVFP4G_EINVAL;
-  const int64_t ntm = (n + kBM - 1) / kBM, ntn = (k + kBN - 1) / kBN;
-  if (ntm * ntn * num_experts > (int64_t)INT32_MAX) return NVFP4G_EINVAL;
-  int rc = check_gemm_ptrs(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax, out);
+  int rc = check_wgrad(sum_m, n, k, num_experts);
   if (rc) return rc;
+  if ((rc = check_gemm_ptrs(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax, out))) return rc;
   Routing R;
   R.num_experts = num_experts;
   R.m_capacity = (int32_t)sum_m;
@@ -443,10 +458,27 @@ int nvfp4_group_gemm_wgrad(const uint8_t* a_col_data, const uint8_t* a_col_scale
   for (int32_t e = 0; e < num_experts; ++e) order.e[e] = (uint16_t)e;
   std::stable_sort(order.e, order.e + num_experts,
                    [&](uint16_t a, uint16_t b) { return h_splits[a] > h_splits[b]; });
-  hipLaunchKernelGGL(gemm_wgrad_kernel, dim3((uint32_t)(ntm * ntn * num_experts)), dim3(kThreads), 0,
-                     (hipStream_t)stream, a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax,
-                     n, k, R, order, (uint32_t)ntm, (uint32_t)ntn, out);
-  return hip_status();
+  return launch_wgrad(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax, n, k, R, order,
+                      true, out, (hipStream_t)stream);
+}
+
+int nvfp4_group_gemm_wgrad_graphsafe(const uint8_t* a_col_data, const uint8_t* a_col_scale,
+                                     const float* a_col_amax, const uint8_t* b_col_data,
+                                     const uint8_t* b_col_scale, const float* b_col_amax, int64_t m_capacity,
+                                     int64_t n, int64_t k, int32_t num_experts, const int32_t* d_offs, float* out,
+                                     int32_t* d_status, void* stream) {
+  int rc = check_wgrad(m_capacity, n, k, num_experts);
+  if (rc) return rc;
+  // the routing is only known on the device: bound every expert by the capacity
+  if (m_capacity > kGemmMaxExpertRows) return NVFP4G_EINVAL;
+  if ((rc = check_gemm_ptrs(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax, out))) return rc;
+  Routing R;
+  R.num_experts = num_experts;
+  R.m_capacity = (int32_t)m_capacity;
+  if ((rc = graph_routing(d_offs, d_status, num_experts, m_capacity, &R))) return rc;
+  ExpertOrder order;  // unused: experts in index order
+  return launch_wgrad(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax, n, k, R, order,
+                      false, out, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -217,3 +217,43 @@ def test_fwd_random_operand_bytes():
     want, bound = O.group_gemm(*a, b[0].reshape(E, n, -1), b[1].reshape(E, n, -1), b[2], splits, n, k)
     out = run_fwd(a, b, splits, n, k)
     check_close(out.numpy(), want, bound, k, "fwd random bytes")
+
+
+def test_wgrad_graphsafe_equals_host_split_and_replays():
+    # the graph-safe weight gradient equals the host-split one bit for bit, and
+    # one hipGraph capture replays under new routing written to the offsets
+    rng = np.random.default_rng(92)
+    n, k, e_n, m_cap = 48, 160, 4, 1024
+    yd = rng.integers(0, 256, m_cap * n // 2, dtype=np.uint8)
+    ys = rng.integers(0x20, 0x50, m_cap * n // 16, dtype=np.uint8)
+    xd = rng.integers(0, 256, m_cap * k // 2, dtype=np.uint8)
+    xs = rng.integers(0x20, 0x50, m_cap * k // 16, dtype=np.uint8)
+    ya = rng.uniform(0.5, 2.0, e_n * n).astype(np.float32)
+    xa = rng.uniform(0.5, 2.0, e_n * k).astype(np.float32)
+    ops = [dev(v) for v in (yd, ys, ya, xd, xs, xa)]
+    d_offs = torch.zeros(e_n, dtype=torch.int32, device="cuda:0")
+    d_status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    out = torch.zeros((e_n, n, k), dtype=torch.float32, device="cuda:0")
+    routes = [[256, 0, 512, 256], [128, 384, 0, 128], [0, 0, 0, 1024], [256, 256, 256, 256]]
+    d_offs.copy_(torch.tensor(B.offsets_from_splits(routes[0]), dtype=torch.int32))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.nvfp4_group_gemm_wgrad_graphsafe(*ops, m_cap, e_n, d_offs, n, k, out, d_status)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.nvfp4_group_gemm_wgrad_graphsafe(*ops, m_cap, e_n, d_offs, n, k, out, d_status)
+    torch.cuda.synchronize()
+    for i, sp in enumerate(routes):
+        total = sum(sp)
+        d_offs.copy_(torch.tensor(B.offsets_from_splits(sp), dtype=torch.int32))
+        out.fill_(np.nan)
+        g.replay()
+        ref = torch.empty((e_n, n, k), dtype=torch.float32, device="cuda:0")
+        B.nvfp4_group_gemm_wgrad(ops[0][:total * n // 2], ops[1][:total * n // 16], ops[2],
+                                 ops[3][:total * k // 2], ops[4][:total * k // 16], ops[5], sp, n, k, ref)
+        torch.cuda.synchronize()
+        assert int(d_status.item()) == 0
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {i}"
+        log(f"wgrad replay {i}: routing {sp} byte-identical to the host-split call")

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
         "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
         "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
         "nvfp4_group_gemm", "nvfp4_group_gemm_graphsafe", "nvfp4_group_gemm_wgrad",
-        "nvfp4_group_strerror",
+        "nvfp4_group_gemm_wgrad_graphsafe", "nvfp4_group_strerror",
     }
 
 
@@ -180,3 +180,9 @@ def test_gemm_host_checks(lib):
     assert w(*ok, 256, 24, 32, 2, sp, FAKE, None) == -1            # n not a multiple of 16
     assert w(*ok, 256, 32, 40, 2, sp, FAKE, None) == -1            # k not a multiple of 16
     assert w(*ok, 228, 32, 32, 2, bad, FAKE, None) == -2           # split not a multiple of 128
+    wg = lib.nvfp4_group_gemm_wgrad_graphsafe
+    wg.restype = ctypes.c_int
+    wg.argtypes = g.argtypes
+    assert wg(*ok, 256, 32, 32, 2, None, FAKE, FAKE, None) == -1  # no device offsets
+    assert wg(*ok, 256, 32, 32, 2, FAKE, FAKE, None, None) == -1  # no status word
+    assert wg(*ok, 1 << 23, 32, 32, 2, FAKE, FAKE, FAKE, None) == -1  # capacity above 2^22 rows
