@@ -37,6 +37,9 @@
 //    the exact E2M1 values two at a time, one packed fp16 multiply applies
 //    value(S) (converted once per block pair by v_cvt_scalef32_pk_f16_fp8).
 //  * Global loads are buffer loads: lines beyond an operand read as zero.
+//    The 16-byte granules of a line are XOR-swizzled in LDS so that a
+//    fragment read (32 consecutive lines, same granule) spreads over the
+//    banks.
 //  * Tile order: groups of 8 row tiles sweep the column tiles together, and
 //    super-tiles of 64 tiles are dealt round-robin to the 8 XCDs, so each XCD
 //    shares operand slices through its L2 and the XCDs share the work evenly.
@@ -103,7 +106,7 @@ __device__ __forceinline__ void grouped_tile(uint32_t t, uint32_t ntm, uint32_t 
 constexpr uint32_t kRowBytes = kBK / 2, kRowScales = kBK / 16;
 constexpr uint32_t kStA = 0, kStB = kBM * kRowBytes, kStAS = kStB + kBN * kRowBytes,
                    kStBS = kStAS + kBM * kRowScales;
-constexpr uint32_t kStageBytes = kStBS + kBN * kRowScales;  // 46080
+constexpr uint32_t kStageBytes = kStBS + kBN * kRowScales;  // 27 KB
 // copies per thread per stage (direct global -> LDS loads): 16-byte code
 // granules of A and B, 4-byte scale words of A and B
 constexpr int kCpA = kBM * kRowBytes / 16 / kThreads, kCpB = kBN * kRowBytes / 16 / kThreads;
