@@ -107,7 +107,7 @@ def algorithmic_bytes(sum_m: int, k: int, E: int, rowwise: bool, columnwise: boo
     return {"amax_kernel": amax_k, "cast_kernel": cast_k, "step": amax_k + cast_k}
 
 
-def cpu_baseline(w, target_rows: int = 6144) -> dict:
+def cpu_baseline(w, target_rows: int = 16384) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload:
     whole experts (in expert order, skipping any that would overshoot) up to
     ``target_rows`` rows, both directions, one thread."""
