@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kThreads) void mxfp4_group_cast_kernel(
     uint8_t* __restrict__ col_data, uint8_t* __restrict__ col_scale) {
   __shared__ uint32_t l_rs[kTileRows][kTileCols / 128];  // row scales, 8 per row
   __shared__ uint32_t l_cs[kTileCols];                   // column scales, 4 per column
+  __shared__ uint32_t l_rd[kTileRows][kTileCols / 8];    // row data, 128 bytes per row (swizzled)
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
   const TileCoord tc = tile_coord(nrow_tiles);
@@ -91,8 +92,6 @@ __global__ __launch_bounds__(kThreads) void mxfp4_group_cast_kernel(
       r = pkmax(r, swap8(r));
       rp[p] = swap16_max(r, r);
     }
-    const rsrc_t rd = make_rsrc(row_data + (int64_t)row0 * (k / 2) + col_base / 2);
-    const uint32_t vo = active ? 16u * rb * (ku / 2) + lcol / 2 : kOutOfRange;
     const int q = cg & 3;  // the four lanes of a block share its scale writes
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -103,7 +102,10 @@ __global__ __launch_bounds__(kThreads) void mxfp4_group_cast_kernel(
       packed = FP4X2(packed, bf16lo(v[i][1]) * m, bf16hi(v[i][1]) * m, 1);
       packed = FP4X2(packed, bf16lo(v[i][2]) * m, bf16hi(v[i][2]) * m, 2);
       packed = FP4X2(packed, bf16lo(v[i][3]) * m, bf16hi(v[i][3]) * m, 3);
-      __builtin_amdgcn_raw_buffer_store_b32(packed, rd, vo, (uint32_t)i * (ku / 2), kStoreAux);
+      // bytes lcol/2 .. +3 of row 16*rb + i: dword 8*wave + cg; granule q
+      // of row r sits at slot q ^ ((r / 16) % 8), so the wave's writes (eight
+      // rows 16 apart, same dword column) fall in distinct banks
+      l_rd[16 * rb + i][(8 * wave + cg) ^ (rb << 2)] = packed;
       if ((i & 3) == q)
         reinterpret_cast<uint8_t*>(&l_rs[16 * rb + i][0])[wave * 2 + (cg >> 2)] = (uint8_t)byte;
     }
@@ -143,8 +145,21 @@ __global__ __launch_bounds__(kThreads) void mxfp4_group_cast_kernel(
     }
   }
 
-  // scales: staged in LDS, then one store per row (8 bytes) / column (4 bytes)
+  // rowwise data and scales: staged in LDS, then one store per 16-byte
+  // granule of a row line, one per row (8 scale bytes) / column (4 bytes)
   __syncthreads();
+  if (row_data) {
+    // thread t writes granule t % 8 (32 columns; ncols is a multiple of 32)
+    // of rows t / 8 + 32 * it
+    const rsrc_t rd = make_rsrc(row_data + (int64_t)row0 * (k / 2) + col_base / 2);
+    const uint32_t g = tid & 7;
+#pragma unroll
+    for (int it = 0; it < kTileRows / 32; ++it) {
+      const uint32_t r = 32 * it + (tid >> 3);
+      const u32x4 v4 = *reinterpret_cast<const u32x4*>(&l_rd[r][4 * (g ^ ((r >> 4) & 7))]);
+      if (32 * g < ncols) __builtin_amdgcn_raw_buffer_store_b128(v4, rd, r * (ku / 2) + 16 * g, 0, kStoreAux);
+    }
+  }
   if (row_data && tid < kTileRows) {
     uint8_t* dst = row_scale + ((int64_t)row0 + tid) * (k / 32) + col_base / 32;
     if (ncols == kTileCols && (k & 255) == 0) {
@@ -171,16 +186,18 @@ int check_mx(const void* x, int64_t rows, int64_t k, int32_t E, Routing* R, cons
   return NVFP4G_OK;
 }
 
-// Residency cap: at most two work-groups (two tiles in flight) per CU.  The
-// kernel needs 90 VGPRs (five waves per SIMD), but with that many tiles in
-// flight the interleaved row and transposed stores run the HBM slower: on
-// the 32-expert K=7168 sum_M=65536 workload one launch takes ~388 us
-// uncapped, ~355 us at three and ~325 us at two work-groups per CU (one is
-// slower again, ~399 us).  Reserving half of the CU's 160 KB of LDS per
-// work-group (dynamic LDS the kernel does not touch) enforces the cap.
+// Residency cap: at most four work-groups (four tiles in flight) per CU.
+// The kernel needs 94 VGPRs (five waves per SIMD).  On the 32-expert K=7168
+// sum_M=65536 workload one launch takes ~315 us at three work-groups per CU
+// and ~266-276 us at four or five; before the rowwise data was staged in LDS
+// (four 32-byte pieces per 128-byte line instead of one 16-byte store per
+// granule) more tiles in flight made it slower, and the cap was two.
+// Reserving a quarter of the CU's 160 KB of LDS per work-group (dynamic LDS
+// the kernel does not touch) enforces the cap.
 constexpr size_t kLdsPerCu = 160 * 1024;
-constexpr int kMxGroupsPerCu = 2;
-constexpr size_t kMxStaticLds = kTileRows * (kTileCols / 128) * 4 + kTileCols * 4;  // l_rs + l_cs
+constexpr int kMxGroupsPerCu = 4;
+constexpr size_t kMxStaticLds =
+    kTileRows * (kTileCols / 128) * 4 + kTileCols * 4 + kTileRows * (kTileCols / 8) * 4;  // l_rs + l_cs + l_rd
 constexpr size_t kMxLdsReserve = kLdsPerCu / kMxGroupsPerCu - kMxStaticLds;
 
 int launch_mx(const uint16_t* x, int64_t rows, int64_t k, const Routing& R, uint8_t* row_data,

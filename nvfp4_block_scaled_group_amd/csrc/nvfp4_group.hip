@@ -184,6 +184,13 @@ __global__ __launch_bounds__(kThreads) void group_amax_kernel(
 
 // Grouped cast of one 128 x 256 tile; rowwise and/or columnwise.
 //
+// Rowwise data is staged in LDS and written a whole 128-byte row line per
+// eight lanes (16 bytes each): written straight from the lane layout, a line
+// would be assembled from four waves' 32-byte pieces, four times the store
+// requests.  In LDS, the 16-byte granule q of row r sits at slot
+// q ^ ((r / 16) % 8), so the 4-byte writes of a wave (lanes on eight rows
+// 16 apart, same dword column) fall in distinct banks.
+//
 // Addressing: every tensor is reached through a raw buffer descriptor whose
 // base is the tile's first element, a per-lane 32-bit offset and a scalar
 // per-row (or per-column) offset, so no per-store 64-bit address arithmetic
@@ -199,6 +206,7 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
   __shared__ float2 l_col[kTileCols];                   // (s, 1/s) per column of the tile
   __shared__ uint32_t l_rs[kTileRows][kTileCols / 64];  // row scales, 16 per row
   __shared__ uint32_t l_cs[kTileCols][2];               // column scales, 8 per column
+  __shared__ uint32_t l_rd[kTileRows][kTileCols / 8];   // row data, 128 bytes per row (swizzled)
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
   const TileCoord tc = tile_coord(nrow_tiles);
@@ -232,41 +240,39 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
     __syncthreads();
 
     if (row_data) {
-      // block amax of each of the lane's 16 rows over 16 columns (own 8 + lane^8)
-      uint32_t b16[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t a = pkmax(pkmax(v[i][0] & 0x7FFF7FFFu, v[i][1] & 0x7FFF7FFFu),
-                                 pkmax(v[i][2] & 0x7FFF7FFFu, v[i][3] & 0x7FFF7FFFu));
-        b16[i] = hmax(a);
-        b16[i] = max(b16[i], swap8(b16[i]));
-      }
-      // the lane pair shares each block: the even lane derives the scales of
-      // rows 0..7, the odd lane those of rows 8..15, then they swap
+      // The lane pair (lane, lane^8) holds the two 8-column halves of each
+      // 16-column block of its 16 rows.  Iteration i serves rows i and 8+i:
+      // the even lane derives the scale of row i, the odd lane that of row
+      // 8+i; each sends the partner the half amax it needs, then the two
+      // multipliers are swapped back, and both rows are encoded.
       const bool odd = cg & 1;
-      float mrow[16];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = hmax(pkmax(pkmax(v[i][0] & 0x7FFF7FFFu, v[i][1] & 0x7FFF7FFFu),
+                                       pkmax(v[i][2] & 0x7FFF7FFFu, v[i][3] & 0x7FFF7FFFu)));
+        const uint32_t hi = hmax(pkmax(pkmax(v[8 + i][0] & 0x7FFF7FFFu, v[8 + i][1] & 0x7FFF7FFFu),
+                                       pkmax(v[8 + i][2] & 0x7FFF7FFFu, v[8 + i][3] & 0x7FFF7FFFu)));
+        const uint32_t b16 = max(odd ? hi : lo, swap8(odd ? lo : hi));
         const int ri = odd ? 8 + i : i;
         const float2 sl = l_row[16 * rb + ri];
         float m;
-        const uint32_t S = block_step(__uint_as_float((odd ? b16[8 + i] : b16[i]) << 16), sl.x, sl.y, &m);
+        const uint32_t S = block_step(__uint_as_float(b16 << 16), sl.x, sl.y, &m);
         const float mo = __uint_as_float(swap8(__float_as_uint(m)));
-        mrow[i] = odd ? mo : m;
-        mrow[8 + i] = odd ? m : mo;
         reinterpret_cast<uint8_t*>(&l_rs[16 * rb + ri][0])[wave * 4 + (cg >> 1)] = (uint8_t)S;
-      }
-      const rsrc_t rd = make_rsrc(row_data + (int64_t)row0 * (k / 2) + col_base / 2);
-      const uint32_t vo = active ? 16u * rb * (ku / 2) + lcol / 2 : kOutOfRange;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float m = mrow[i];
+        // bytes lcol/2 .. +3 of row 16*rb + r: dword 8*wave + cg, swizzled
+        const float m_lo = odd ? mo : m, m_hi = odd ? m : mo;
         uint32_t packed = 0;
-        packed = FP4X2(packed, bf16lo(v[i][0]) * m, bf16hi(v[i][0]) * m, 0);
-        packed = FP4X2(packed, bf16lo(v[i][1]) * m, bf16hi(v[i][1]) * m, 1);
-        packed = FP4X2(packed, bf16lo(v[i][2]) * m, bf16hi(v[i][2]) * m, 2);
-        packed = FP4X2(packed, bf16lo(v[i][3]) * m, bf16hi(v[i][3]) * m, 3);
-        __builtin_amdgcn_raw_buffer_store_b32(packed, rd, vo, (uint32_t)i * (ku / 2), kStoreAux);
+        packed = FP4X2(packed, bf16lo(v[i][0]) * m_lo, bf16hi(v[i][0]) * m_lo, 0);
+        packed = FP4X2(packed, bf16lo(v[i][1]) * m_lo, bf16hi(v[i][1]) * m_lo, 1);
+        packed = FP4X2(packed, bf16lo(v[i][2]) * m_lo, bf16hi(v[i][2]) * m_lo, 2);
+        packed = FP4X2(packed, bf16lo(v[i][3]) * m_lo, bf16hi(v[i][3]) * m_lo, 3);
+        l_rd[16 * rb + i][(8 * wave + cg) ^ (rb << 2)] = packed;
+        packed = 0;
+        packed = FP4X2(packed, bf16lo(v[8 + i][0]) * m_hi, bf16hi(v[8 + i][0]) * m_hi, 0);
+        packed = FP4X2(packed, bf16lo(v[8 + i][1]) * m_hi, bf16hi(v[8 + i][1]) * m_hi, 1);
+        packed = FP4X2(packed, bf16lo(v[8 + i][2]) * m_hi, bf16hi(v[8 + i][2]) * m_hi, 2);
+        packed = FP4X2(packed, bf16lo(v[8 + i][3]) * m_hi, bf16hi(v[8 + i][3]) * m_hi, 3);
+        l_rd[16 * rb + 8 + i][(8 * wave + cg) ^ (rb << 2)] = packed;
       }
     }
 
@@ -298,8 +304,23 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
       }
     }
 
-    // scales: staged in LDS, then one wide store per row / per column
+    // rowwise data and scales: staged in LDS, then wide stores per line
     __syncthreads();
+    if (row_data) {
+      // thread t writes granule t % 8 (32 columns) of rows t / 8 + 32 * it;
+      // a granule of a ragged last chunk may hold only 16 valid columns
+      const rsrc_t rd = make_rsrc(row_data + (int64_t)row0 * (k / 2) + col_base / 2);
+      const uint32_t g = tid & 7;
+#pragma unroll
+      for (int it = 0; it < kTileRows / 32; ++it) {
+        const uint32_t r = 32 * it + (tid >> 3);
+        const u32x4 q = *reinterpret_cast<const u32x4*>(&l_rd[r][4 * (g ^ ((r >> 4) & 7))]);
+        if (32 * g + 32 <= ncols)
+          __builtin_amdgcn_raw_buffer_store_b128(q, rd, r * (ku / 2) + 16 * g, 0, kStoreAux);
+        else if (32 * g < ncols)
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, rd, r * (ku / 2) + 16 * g, 0, kStoreAux);
+      }
+    }
     if (row_data && tid < kTileRows) {
       uint8_t* dst = row_scale + ((int64_t)row0 + tid) * (k / 16) + col_base / 16;
       if (ncols == kTileCols && (k & 255) == 0) {
