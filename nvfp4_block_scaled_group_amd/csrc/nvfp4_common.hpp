@@ -110,6 +110,12 @@ constexpr int kStoreAux = NVFP4G_STORE_AUX;
 // the rowwise data and for the small scale stores).
 constexpr int kStoreStream = 2;
 
+// Compile-time flag passed to a generic lambda (one instantiation per value).
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 // ------------------------------------------------------------- tiles
 
 // Tile order of the cast kernel.  Work-groups are dispatched round-robin

@@ -207,6 +207,7 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
   __shared__ uint32_t l_rs[kTileRows][kTileCols / 64];  // row scales, 16 per row
   __shared__ uint32_t l_cs[kTileCols][2];               // column scales, 8 per column
   __shared__ uint32_t l_rd[kTileRows][kTileCols / 8];   // row data, 128 bytes per row (swizzled)
+  __shared__ uint32_t l_slow[kThreads / 64];            // per wave: a line needs the exact block step
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
   const TileCoord tc = tile_coord(nrow_tiles);
@@ -229,80 +230,98 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
 
     uint32_t v[16][4];
     load_tile(x + (int64_t)row0 * k + col_base, ku, vo_x, v);
+    bool slow_line = false;
     if (row_data && tid < kTileRows) {
       const float s = row_amax[row0 + tid] / 2688.0f;
       l_row[tid] = make_float2(s, 1.0f / s);
+      slow_line = !(s >= kFastMinLineScale);
     }
     if (col_data) {
       const float s = (uint32_t)tid < ncols ? col_amax[(int64_t)e * k + col_base + tid] / 2688.0f : 0.0f;
       l_col[tid] = make_float2(s, 1.0f / s);
+      slow_line = slow_line || ((uint32_t)tid < ncols && !(s >= kFastMinLineScale));
     }
+    const bool wave_slow = __ballot(slow_line) != 0;
+    if (lane == 0) l_slow[wave] = wave_slow;
     __syncthreads();
+    // When every line of the tile has s >= 2^-112 (the usual case) the block
+    // steps take the fast path without a per-lane test; otherwise each block
+    // step picks its path from its own line scale.
+    const bool all_fast = uni((uint32_t)(l_slow[0] | l_slow[1] | l_slow[2] | l_slow[3])) == 0u;
 
-    if (row_data) {
-      // The lane pair (lane, lane^8) holds the two 8-column halves of each
-      // 16-column block of its 16 rows.  Iteration i serves rows i and 8+i:
-      // the even lane derives the scale of row i, the odd lane that of row
-      // 8+i; each sends the partner the half amax it needs, then the two
-      // multipliers are swapped back, and both rows are encoded.
-      const bool odd = cg & 1;
+    auto encode = [&](auto fast_tag) {
+      constexpr bool kAllFast = decltype(fast_tag)::value;
+      if (row_data) {
+        // The lane pair (lane, lane^8) holds the two 8-column halves of each
+        // 16-column block of its 16 rows.  Iteration i serves rows i and 8+i:
+        // the even lane derives the scale of row i, the odd lane that of row
+        // 8+i; each sends the partner the half amax it needs, then the two
+        // multipliers are swapped back, and both rows are encoded.
+        const bool odd = cg & 1;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = hmax(pkmax(pkmax(v[i][0] & 0x7FFF7FFFu, v[i][1] & 0x7FFF7FFFu),
-                                       pkmax(v[i][2] & 0x7FFF7FFFu, v[i][3] & 0x7FFF7FFFu)));
-        const uint32_t hi = hmax(pkmax(pkmax(v[8 + i][0] & 0x7FFF7FFFu, v[8 + i][1] & 0x7FFF7FFFu),
-                                       pkmax(v[8 + i][2] & 0x7FFF7FFFu, v[8 + i][3] & 0x7FFF7FFFu)));
-        const uint32_t b16 = max(odd ? hi : lo, swap8(odd ? lo : hi));
-        const int ri = odd ? 8 + i : i;
-        const float2 sl = l_row[16 * rb + ri];
-        float m;
-        const uint32_t S = block_step(__uint_as_float(b16 << 16), sl.x, sl.y, &m);
-        const float mo = __uint_as_float(swap8(__float_as_uint(m)));
-        reinterpret_cast<uint8_t*>(&l_rs[16 * rb + ri][0])[wave * 4 + (cg >> 1)] = (uint8_t)S;
-        // bytes lcol/2 .. +3 of row 16*rb + r: dword 8*wave + cg, swizzled
-        const float m_lo = odd ? mo : m, m_hi = odd ? m : mo;
-        uint32_t packed = 0;
-        packed = FP4X2(packed, bf16lo(v[i][0]) * m_lo, bf16hi(v[i][0]) * m_lo, 0);
-        packed = FP4X2(packed, bf16lo(v[i][1]) * m_lo, bf16hi(v[i][1]) * m_lo, 1);
-        packed = FP4X2(packed, bf16lo(v[i][2]) * m_lo, bf16hi(v[i][2]) * m_lo, 2);
-        packed = FP4X2(packed, bf16lo(v[i][3]) * m_lo, bf16hi(v[i][3]) * m_lo, 3);
-        l_rd[16 * rb + i][(8 * wave + cg) ^ (rb << 2)] = packed;
-        packed = 0;
-        packed = FP4X2(packed, bf16lo(v[8 + i][0]) * m_hi, bf16hi(v[8 + i][0]) * m_hi, 0);
-        packed = FP4X2(packed, bf16lo(v[8 + i][1]) * m_hi, bf16hi(v[8 + i][1]) * m_hi, 1);
-        packed = FP4X2(packed, bf16lo(v[8 + i][2]) * m_hi, bf16hi(v[8 + i][2]) * m_hi, 2);
-        packed = FP4X2(packed, bf16lo(v[8 + i][3]) * m_hi, bf16hi(v[8 + i][3]) * m_hi, 3);
-        l_rd[16 * rb + 8 + i][(8 * wave + cg) ^ (rb << 2)] = packed;
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t lo = hmax(pkmax(pkmax(v[i][0] & 0x7FFF7FFFu, v[i][1] & 0x7FFF7FFFu),
+                                         pkmax(v[i][2] & 0x7FFF7FFFu, v[i][3] & 0x7FFF7FFFu)));
+          const uint32_t hi = hmax(pkmax(pkmax(v[8 + i][0] & 0x7FFF7FFFu, v[8 + i][1] & 0x7FFF7FFFu),
+                                         pkmax(v[8 + i][2] & 0x7FFF7FFFu, v[8 + i][3] & 0x7FFF7FFFu)));
+          const uint32_t b16 = max(odd ? hi : lo, swap8(odd ? lo : hi));
+          const int ri = odd ? 8 + i : i;
+          const float2 sl = l_row[16 * rb + ri];
+          float m;
+          const uint32_t S = kAllFast ? block_scale_fast(__uint_as_float(b16 << 16), sl.x, sl.y, &m)
+                                      : block_step(__uint_as_float(b16 << 16), sl.x, sl.y, &m);
+          const float mo = __uint_as_float(swap8(__float_as_uint(m)));
+          reinterpret_cast<uint8_t*>(&l_rs[16 * rb + ri][0])[wave * 4 + (cg >> 1)] = (uint8_t)S;
+          // bytes lcol/2 .. +3 of row 16*rb + r: dword 8*wave + cg, swizzled
+          const float m_lo = odd ? mo : m, m_hi = odd ? m : mo;
+          uint32_t packed = 0;
+          packed = FP4X2(packed, bf16lo(v[i][0]) * m_lo, bf16hi(v[i][0]) * m_lo, 0);
+          packed = FP4X2(packed, bf16lo(v[i][1]) * m_lo, bf16hi(v[i][1]) * m_lo, 1);
+          packed = FP4X2(packed, bf16lo(v[i][2]) * m_lo, bf16hi(v[i][2]) * m_lo, 2);
+          packed = FP4X2(packed, bf16lo(v[i][3]) * m_lo, bf16hi(v[i][3]) * m_lo, 3);
+          l_rd[16 * rb + i][(8 * wave + cg) ^ (rb << 2)] = packed;
+          packed = 0;
+          packed = FP4X2(packed, bf16lo(v[8 + i][0]) * m_hi, bf16hi(v[8 + i][0]) * m_hi, 0);
+          packed = FP4X2(packed, bf16lo(v[8 + i][1]) * m_hi, bf16hi(v[8 + i][1]) * m_hi, 1);
+          packed = FP4X2(packed, bf16lo(v[8 + i][2]) * m_hi, bf16hi(v[8 + i][2]) * m_hi, 2);
+          packed = FP4X2(packed, bf16lo(v[8 + i][3]) * m_hi, bf16hi(v[8 + i][3]) * m_hi, 3);
+          l_rd[16 * rb + 8 + i][(8 * wave + cg) ^ (rb << 2)] = packed;
+        }
       }
-    }
 
-    if (col_data) {
-      const rsrc_t cd = make_rsrc(col_data + k * (int64_t)rbeg / 2 + col_base * (me / 2) + (row0 - rbeg) / 2);
-      const uint32_t vo = active ? lcol * (me / 2) + 8u * rb : kOutOfRange;
+      if (col_data) {
+        const rsrc_t cd = make_rsrc(col_data + k * (int64_t)rbeg / 2 + col_base * (me / 2) + (row0 - rbeg) / 2);
+        const uint32_t vo = active ? lcol * (me / 2) + 8u * rb : kOutOfRange;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t mx = 0;
+        for (int j = 0; j < 8; ++j) {
+          uint32_t mx = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = pkmax(mx, v[i][j >> 1] & 0x7FFF7FFFu);
-        const uint32_t b16 = (j & 1) ? (mx >> 16) : (mx & 0xFFFFu);
-        const float2 sl = l_col[lcol + j];
-        float m;
-        const uint32_t S = block_step(__uint_as_float(b16 << 16), sl.x, sl.y, &m);
-        reinterpret_cast<uint8_t*>(&l_cs[lcol + j][0])[rb] = (uint8_t)S;
+          for (int i = 0; i < 16; ++i) mx = pkmax(mx, v[i][j >> 1] & 0x7FFF7FFFu);
+          const uint32_t b16 = (j & 1) ? (mx >> 16) : (mx & 0xFFFFu);
+          const float2 sl = l_col[lcol + j];
+          float m;
+          const uint32_t S = kAllFast ? block_scale_fast(__uint_as_float(b16 << 16), sl.x, sl.y, &m)
+                                      : block_step(__uint_as_float(b16 << 16), sl.x, sl.y, &m);
+          reinterpret_cast<uint8_t*>(&l_cs[lcol + j][0])[rb] = (uint8_t)S;
 #define XCOL(i) (((j & 1) ? bf16hi(v[i][j >> 1]) : bf16lo(v[i][j >> 1])) * m)
-        uint32_t lo = 0, hi = 0;
-        lo = FP4X2(lo, XCOL(0), XCOL(1), 0);
-        lo = FP4X2(lo, XCOL(2), XCOL(3), 1);
-        lo = FP4X2(lo, XCOL(4), XCOL(5), 2);
-        lo = FP4X2(lo, XCOL(6), XCOL(7), 3);
-        hi = FP4X2(hi, XCOL(8), XCOL(9), 0);
-        hi = FP4X2(hi, XCOL(10), XCOL(11), 1);
-        hi = FP4X2(hi, XCOL(12), XCOL(13), 2);
-        hi = FP4X2(hi, XCOL(14), XCOL(15), 3);
+          uint32_t lo = 0, hi = 0;
+          lo = FP4X2(lo, XCOL(0), XCOL(1), 0);
+          lo = FP4X2(lo, XCOL(2), XCOL(3), 1);
+          lo = FP4X2(lo, XCOL(4), XCOL(5), 2);
+          lo = FP4X2(lo, XCOL(6), XCOL(7), 3);
+          hi = FP4X2(hi, XCOL(8), XCOL(9), 0);
+          hi = FP4X2(hi, XCOL(10), XCOL(11), 1);
+          hi = FP4X2(hi, XCOL(12), XCOL(13), 2);
+          hi = FP4X2(hi, XCOL(14), XCOL(15), 3);
 #undef XCOL
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, cd, vo, (uint32_t)j * (me / 2), kStoreStream);
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, cd, vo, (uint32_t)j * (me / 2), kStoreStream);
+        }
       }
-    }
+    };
+    if (all_fast)
+      encode(BoolTag<true>{});
+    else
+      encode(BoolTag<false>{});
 
     // rowwise data and scales: staged in LDS, then wide stores per line
     __syncthreads();

@@ -78,24 +78,19 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 // ---------------------------------------------------------------- numerics
 
 // E4M3FN code of t >= 0 (finite or +inf): nearest, ties to even, saturating
-// at 448 (0x7E).  Normal range: round the fp32 mantissa to 3 bits and
-// re-bias the exponent (7 - 127); subnormal range (t < 2^-6): the nearest
-// multiple of 2^-9, found by adding 2^14 (whose fp32 spacing is 2^-9).
+// at 448 (0x7E).  gfx950's v_cvt_pk_fp8_f32 (OCP E4M3FN) rounds to nearest
+// with ties to even and, checked on the hardware against the plain rule
+// (round the fp32 mantissa to 3 bits and re-bias the exponent by 7 - 127;
+// below 2^-6 the nearest multiple of 2^-9) over every fp32 t in [0, 464),
+// gives the same code; it does not saturate, so t is clamped at 448 first
+// (every t >= 448 then encodes as 0x7E, as the rule says).
 __device__ __forceinline__ uint32_t e4m3_code(float t) {
-  if (t >= 448.0f) return 0x7Eu;
-  const uint32_t tb = __float_as_uint(t);
-  if (tb >= 0x3C800000u) {  // t >= 2^-6
-    const uint32_t r = (tb + 0x7FFFFu + ((tb >> 20) & 1u)) >> 20;
-    return r - (120u << 3);
-  }
-  return __float_as_uint(t + 16384.0f) - 0x46800000u;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = c >> 3, f = c & 7u;
-  return e ? __uint_as_float(((e + 120u) << 23) | (f << 20))
-           : (float)f * 0.001953125f;  // f * 2^-9, exact
-}
+// value(c) of an E4M3FN code (0 .. 0x7E), exact: v_cvt_f32_fp8, checked on
+// the hardware against  e ? 2^(e-7) * (1 + f/8) : f * 2^-9  for every code.
+__device__ __forceinline__ float e4m3_value(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 
 // Block step: E4M3 scale code of a block with amax b on a line with scale s,
 // and the element multiplier m = 1 / (value(S) * s).

@@ -4,6 +4,8 @@
 //
 //  * the hardware FP4 convert (FP4X2, scale 1.0) against the software E2M1
 //    rule (e2m1_code) on every non-NaN fp32 pattern, both nibble positions;
+//  * the hardware E4M3 encode / decode (e4m3_code, e4m3_value) against the
+//    plain E4M3FN rule on every fp32 t in [0, +inf] and every finite code;
 //  * the kernels' block step (fast path for line scales >= 2^-112, IEEE
 //    divisions below) against the IEEE-division block step on every pair of
 //    bf16 values b <= A (b = block amax, A = line amax);
@@ -34,6 +36,37 @@ __global__ void fp4_exhaustive_kernel(unsigned long long* counts, uint32_t base)
   atomicAdd(&counts[0], n);
   atomicAdd(&counts[1], bad_lo);
   atomicAdd(&counts[2], bad_hi);
+}
+
+// The plain E4M3FN rule for t >= 0: saturate at 448 (0x7E); t >= 2^-6:
+// round the fp32 mantissa to 3 bits (nearest, ties to even) and re-bias the
+// exponent from 127 to 7; below: the nearest multiple of 2^-9 (ties even),
+// found by adding 2^14, whose fp32 spacing is 2^-9.
+__device__ uint32_t e4m3_code_rule(float t) {
+  if (t >= 448.0f) return 0x7Eu;
+  const uint32_t tb = __float_as_uint(t);
+  if (tb >= 0x3C800000u) return ((tb + 0x7FFFFu + ((tb >> 20) & 1u)) >> 20) - (120u << 3);
+  return __float_as_uint(t + 16384.0f) - 0x46800000u;
+}
+// value of an E4M3FN code: e ? 2^(e-7) * (1 + f/8) : f * 2^-9
+__device__ float e4m3_value_rule(uint32_t c) {
+  const uint32_t e = c >> 3, f = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (f << 20)) : (float)f * 0.001953125f;
+}
+
+__global__ void e4m3_exhaustive_kernel(unsigned long long* counts) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  unsigned long long n = 0, bad = 0;
+  for (uint32_t p = blockIdx.x * blockDim.x + threadIdx.x; p <= 0x7F800000u; p += stride) {
+    const float t = __uint_as_float(p);
+    n++;
+    bad += e4m3_code(t) != e4m3_code_rule(t);
+  }
+  atomicAdd(&counts[0], n);
+  atomicAdd(&counts[1], bad);
+  if (blockIdx.x == 0 && threadIdx.x <= 0x7Eu)
+    atomicAdd(&counts[2], (unsigned long long)(__float_as_uint(e4m3_value(threadIdx.x)) !=
+                                               __float_as_uint(e4m3_value_rule(threadIdx.x))));
 }
 
 // one workgroup per line amax A (bf16 pattern 1..0x7F7F), b over 0..A
@@ -84,6 +117,13 @@ extern "C" {
 int selftest_fp4_exhaustive(unsigned long long* counts) {
   hipLaunchKernelGGL(fp4_exhaustive_kernel, dim3(4096), dim3(256), 0, 0, counts, 0u);
   hipLaunchKernelGGL(fp4_exhaustive_kernel, dim3(4096), dim3(256), 0, 0, counts, 0x80000000u);
+  return status();
+}
+
+// counts (device, 3 x u64, zeroed by the caller): encoded patterns, encode
+// mismatches, decode mismatches.
+int selftest_e4m3_exhaustive(unsigned long long* counts) {
+  hipLaunchKernelGGL(e4m3_exhaustive_kernel, dim3(4096), dim3(256), 0, 0, counts);
   return status();
 }
 

@@ -7,6 +7,8 @@ every input they can receive, and pin GPU outputs to the CPU oracle:
 
 * hardware FP4 convert == the software E2M1 rule, on all 2^32 - 2^24 non-NaN
   fp32 patterns, in both nibble positions;
+* hardware E4M3 encode (clamped at 448) == the plain E4M3FN rule on every fp32
+  t in [0, +inf], and hardware decode == the rule on every finite code;
 * the kernels' block step == the IEEE-division block step, on every pair of
   bf16 values b <= A (532,701,119 pairs: every block amax / line amax pair a
   bf16 input can produce);
@@ -37,6 +39,7 @@ def lib():
     L = ctypes.CDLL(LIB)
     L.selftest_fp4_exhaustive.argtypes = [P]
     L.selftest_block_step_exhaustive.argtypes = [P]
+    L.selftest_e4m3_exhaustive.argtypes = [P]
     L.selftest_block_step_sample.argtypes = [P, P, ctypes.c_int64, P, P]
     L.selftest_fp4_codes.argtypes = [P, ctypes.c_int64, P]
     return L
@@ -53,6 +56,15 @@ def test_fp4_convert_equals_software_rule_on_every_fp32(lib):
     n, bad_lo, bad_hi = c.cpu().tolist()
     assert n == (1 << 32) - 2 * ((1 << 23) - 1)  # all but the NaN patterns
     assert bad_lo == 0 and bad_hi == 0
+
+
+def test_e4m3_convert_equals_plain_rule_on_every_fp32(lib):
+    log("e4m3 convert, all non-negative fp32 patterns")
+    c = torch.zeros(3, dtype=torch.int64, device="cuda:0")
+    assert lib.selftest_e4m3_exhaustive(ptr(c)) == 0
+    n, bad_enc, bad_dec = c.cpu().tolist()
+    assert n == 0x7F800001  # +0 .. +inf
+    assert bad_enc == 0 and bad_dec == 0
 
 
 def test_block_step_equals_ieee_divisions_on_every_bf16_pair(lib):
