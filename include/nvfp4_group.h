@@ -151,6 +151,8 @@ int nvfp4_group_quantize_graphsafe(const uint16_t* x, int64_t m_capacity,
  * recipe", TransformerEngine PR 2931, Important Files Changed: the dequant
  * looks the amax up by the element's row).  Element i of a line with amax A
  * and block scale S:  out = (value(code) * value(S)) * (A / 2688)  (fp32).
+ * Scale bytes are expected to be codes the cast writes (0x00 .. 0x7E); other
+ * bytes give unspecified values (no error is reported).
  *
  * Rowwise: row_data [rows, k/2], row_scale [rows, k/16], row_amax [rows]
  * -> out fp32 [rows, k].  Rows are independent (pass the routed row count). */
