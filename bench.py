@@ -18,6 +18,11 @@ bytes count what the method must move: two reads of x (the column amax needs
 every row of an expert before any of its blocks can be cast), the amax
 vectors written once and read once, and both outputs written once.
 
+``flushed_step`` times the same steps with a 512 MB read before each
+(outside the events), so that the 256 MB memory-side cache holds nothing of
+the step's data; ``cpu_baseline`` is the CPU oracle on a bounded sample,
+timed before the process touches the GPU.
+
 On workloads with both directions the JSON line also carries ``next_rows``:
 the grouped MXFP4 cast of the same input (one read of x, both MXFP4 outputs
 written), the rowwise / columnwise NVFP4 dequant of the step's outputs
@@ -107,10 +112,30 @@ def algorithmic_bytes(sum_m: int, k: int, E: int, rowwise: bool, columnwise: boo
     return {"amax_kernel": amax_k, "cast_kernel": cast_k, "step": amax_k + cast_k}
 
 
-def cpu_baseline(w, target_rows: int = 16384) -> dict:
+_SAMPLE_X = None  # the sample's rows, inherited by the forked oracle workers
+_TASK_ROWS = 1024  # rows per rowwise task
+_TASK_COLS = 1024  # columns per columnwise task
+
+
+def _oracle_task(task) -> None:
+    rowwise, lo, hi, c0, c1 = task
+    from oracle import oracle as O
+    x = _SAMPLE_X[lo:hi] if rowwise else np.ascontiguousarray(_SAMPLE_X[lo:hi, c0:c1])
+    O.group_quantize(x, [hi - lo], rowwise, not rowwise)
+
+
+def cpu_baseline(w, target_rows: int = 16384, max_workers: int = 16) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload:
     whole experts (in expert order, skipping any that would overshoot) up to
-    ``target_rows`` rows, both directions, one thread."""
+    ``target_rows`` rows, both directions.  Timed on one thread (one call),
+    then on the host's cores (at most ``max_workers`` forked processes) as
+    independent oracle calls: the rowwise direction on row ranges and the
+    columnwise direction on column ranges of each expert (rows are
+    independent in the rowwise output and columns in the columnwise one, so
+    together the calls produce the same bytes as the single call).  Runs
+    before the process touches the GPU, so that forking is safe."""
+    global _SAMPLE_X
+    import multiprocessing
     from oracle import oracle as O
     offs = np.concatenate([[0], np.cumsum(w.splits)])
     chosen, rows = [], 0
@@ -122,11 +147,29 @@ def cpu_baseline(w, target_rows: int = 16384) -> dict:
     sp = [int(w.splits[e]) for e in chosen]
     t0 = time.perf_counter()
     O.group_quantize(xs, sp, w.rowwise, w.columnwise)
-    dt = time.perf_counter() - t0
+    dt1 = time.perf_counter() - t0
+    _SAMPLE_X = xs
+    so = np.concatenate([[0], np.cumsum(sp)]).astype(int)
+    tasks = []
+    for i in range(len(sp)):
+        lo, hi = int(so[i]), int(so[i + 1])
+        if w.rowwise:
+            tasks += [(True, r, min(r + _TASK_ROWS, hi), 0, w.k) for r in range(lo, hi, _TASK_ROWS)]
+        if w.columnwise:
+            tasks += [(False, lo, hi, c, min(c + _TASK_COLS, w.k)) for c in range(0, w.k, _TASK_COLS)]
+    tasks.sort(key=lambda t: (t[2] - t[1]) * (t[4] - t[3]), reverse=True)
+    workers = max(1, min(max_workers, os.cpu_count() or 1, len(tasks)))
+    with multiprocessing.get_context("fork").Pool(workers) as pool:
+        t0 = time.perf_counter()
+        list(pool.imap_unordered(_oracle_task, tasks))
+        dtn = time.perf_counter() - t0
+    _SAMPLE_X = None
     b = algorithmic_bytes(rows, w.k, len(sp), w.rowwise, w.columnwise)["step"]
-    return {"value": round(b / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(sp)} whole experts, {rows} of {w.sum_m} rows x K={w.k} "
-                      f"(both directions), single-threaded C oracle, {dt:.2f} s"}
+    return {"value": round(b / dtn / 1e9, 5), "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"{len(sp)} whole experts, {rows} of {w.sum_m} rows x K={w.k} (both directions), "
+                      f"C oracle: {len(tasks)} row-range / column-range calls over {workers} processes "
+                      f"{dtn:.2f} s, one call on one thread {dt1:.2f} s",
+            "value_one_thread": round(b / dt1 / 1e9, 5)}
 
 
 def main():
@@ -143,6 +186,9 @@ def main():
     ap.add_argument("--graph-replays", type=int, default=100)
     ap.add_argument("--next-rows", type=int, default=20,
                     help="launches timed for each of the MXFP4 cast and the two dequants (0: skip)")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="also time the steps with a read of this many MB before each (outside the timed "
+                         "events), so that no input or output is left in the 256 MB memory-side cache (0: skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (3 times, untimed) so that a "
                          "rocprofv3 --pmc run can scale FETCH_SIZE / WRITE_SIZE by a copy of known size")
@@ -152,14 +198,20 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    from nvfp4_block_scaled_group_amd import synth
+
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    w = synth.CONFIGS[args.workload]()
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (before any GPU use)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+
     import torch
     from nvfp4_block_scaled_group_amd import binding as B
-    from nvfp4_block_scaled_group_amd import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
-    w = synth.CONFIGS[args.workload]()
     splits = [int(v) for v in w.splits]
     E, k, m = w.num_experts, w.k, w.sum_m
     x = torch.from_numpy(w.x.view(np.int16)).to(dev)
@@ -245,6 +297,27 @@ def main():
         "kernels": kernels,
     }
 
+    if args.flush_mb > 0:
+        # the same steps with a read of flush_mb MB (twice the 256 MB MALL by
+        # default) before each, outside the events: nothing of x or of the
+        # previous step's outputs is left in the memory-side cache.  A read
+        # (a max reduction) rather than a fill: a fill would leave dirty lines
+        # whose write-back the next step would pay for.
+        flush = torch.ones(args.flush_mb << 17, dtype=torch.int64, device=dev)
+        flush.max()
+        torch.cuda.synchronize()
+        fev = [[tev.new() for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.max()
+            step(fev[i])
+        torch.cuda.synchronize()
+        f_ms = float(np.mean([tev.elapsed_ms(e[0], e[2]) for e in fev]))
+        result["flushed_step"] = {"flush_mb": args.flush_mb, "steps": args.steps,
+                                  "ms_per_step": round(f_ms, 4),
+                                  "GBps": round(nbytes["step"] / (f_ms * 1e-3) / 1e9, 2),
+                                  "unflushed_event_ms_per_step": round(first_ms + second_ms, 4)}
+        del flush
+
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -259,9 +332,8 @@ def main():
     if args.workload == "deepseek_share" and args.graph_replays > 0:
         result["graph_replay"] = graph_replay(B, synth, torch, tev, dev, args.graph_replays)
 
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     tev.close()
     print(json.dumps(result), flush=True)
 
