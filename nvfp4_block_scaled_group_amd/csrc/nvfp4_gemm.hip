@@ -67,7 +67,6 @@ constexpr int kBN = kWavesN * kWN * 32;  // tile columns (j): 256
 static_assert(kBM == 128, "row tiles must be the 128-row expert granule");
 static_assert(kBN % kThreads == 0, "each thread copies whole B lines");
 constexpr int kBK = 128;            // contraction step
-constexpr int kStages = 2;          // LDS stages (double buffer)
 constexpr int kGroupRows = 8;       // row tiles per column sweep
 
 // One NT operand tile: `rows` lines of length L starting at the tile's first
@@ -114,7 +113,6 @@ constexpr int kCpAS = kBM * kRowScales / 4 / kThreads, kCpBS = kBN * kRowScales 
 static_assert(kCpA * 16 * kThreads == kBM * kRowBytes && kCpB * 16 * kThreads == kBN * kRowBytes &&
               kCpAS * 4 * kThreads == kBM * kRowScales && kCpBS * 4 * kThreads == kBN * kRowScales,
               "every thread issues the same copies");
-constexpr uint32_t kLdsBytes = kStages * kStageBytes;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -157,16 +155,18 @@ __device__ __forceinline__ h8_t decode8(uint32_t w, _Float16 S) {
 // eight sub-steps with two 16-byte LDS reads and the four block scales it
 // needs (blocks 4h .. 4h+3) with one 4-byte read.
 //
-// Pipeline (double-buffered LDS): each step starts with the wave waiting
-// for its own copies of the step (issued one step earlier) and a work-group
-// barrier, so the step is complete in LDS and the other stage is no longer
-// being read; every wave then reads all its fragments of the step into
-// registers, issues the direct global -> LDS copies of the next step into the
-// other stage, and multiplies while those copies are in flight.  (LDS reads
-// must come before the next copies are issued: the compiler makes an LDS
-// read wait for every copy in flight.)
+// Pipeline (double-buffered LDS, the two stages in separate arrays): each
+// step starts with the wave waiting for its own copies of the step (issued
+// one step earlier) and a work-group barrier, so the step is complete in LDS
+// and the other stage is no longer being read; every wave then issues the
+// direct global -> LDS copies of the next step into the other stage, reads
+// all its fragments of the step and multiplies while the copies are in
+// flight.  The loop is unrolled by two so that every copy and every read
+// names its stage array: the compiler can then tell that a read of one stage
+// need not wait for copies into the other (with one array and a computed
+// offset it makes every LDS read wait for every copy in flight).
 __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTile& B, uint32_t L,
-                                          f32x16 (&acc)[kWM][kWN], uint8_t* lds) {
+                                          f32x16 (&acc)[kWM][kWN], uint8_t* lds0, uint8_t* lds1) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // every descriptor field is work-group uniform: keep them in scalar registers
   const uint32_t dpitch = uni(L / 2), spitch = uni(L / 16);
@@ -182,8 +182,7 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
 
   // Copy step ks into stage st.  Copy c of a thread moves granule
   // g = c * kThreads + tid; a wave's lanes land contiguously in LDS.
-  auto issue = [&](uint32_t ks, uint32_t st) {
-    uint8_t* base = lds + st * kStageBytes;
+  auto issue = [&](uint32_t ks, uint8_t* base) {
     const uint32_t sd = ks * kRowBytes, ss = ks * kRowScales;
 #pragma unroll
     for (int c = 0; c < kCpA; ++c) {
@@ -212,13 +211,10 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
   };
 
   const int wm = wave / kWavesN, wn = wave % kWavesN, h = lane >> 5;
-  issue(0, 0);
-#pragma unroll 1
-  for (uint32_t ks = 0; ks < nk; ++ks) {
-    const uint32_t st = ks & 1;
+  auto step = [&](uint32_t ks, const uint8_t* base, uint8_t* next) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of step ks
     __syncthreads();
-    const uint8_t* base = lds + st * kStageBytes;
+    if (ks + 1 < nk) issue(ks + 1, next);
     u32x4 wa[kWM][2], wb[kWN][2];
     h2_t sa[kWM][2], sb[kWN][2];
 #pragma unroll
@@ -239,11 +235,9 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
       sb[in][0] = scales_h2(sc & 0xFFFFu);
       sb[in][1] = scales_h2(sc >> 16);
     }
-    if (ks + 1 < nk) issue(ks + 1, st ^ 1);
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
       h8_t af[kWM], bf[kWN];
-      // sub-step s: word s of the lane's 8, block s / 2 of its 4
 #pragma unroll
       for (int im = 0; im < kWM; ++im) af[im] = decode8(wa[im][s >> 2][s & 3], sa[im][s >> 2][(s >> 1) & 1]);
 #pragma unroll
@@ -254,6 +248,13 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
         for (int in = 0; in < kWN; ++in)
           acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[im], bf[in], acc[im][in], 0, 0, 0);
     }
+  };
+  issue(0, lds0);
+#pragma unroll 1
+  for (uint32_t ks = 0; ks < nk; ks += 2) {
+    step(ks, lds0, lds1);
+    if (ks + 1 >= nk) break;
+    step(ks + 1, lds1, lds0);
   }
   // the stages are reused by the epilogue's staging only after every wave is done
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -294,7 +295,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fwd_kernel(
     const uint8_t* __restrict__ a_data, const uint8_t* __restrict__ a_scale, const float* __restrict__ a_amax,
     const uint8_t* __restrict__ b_data, const uint8_t* __restrict__ b_scale, const float* __restrict__ b_amax,
     int64_t n, int64_t k, Routing R, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageBytes];
   __shared__ float lsa[kBM], lsb[kBN];
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fwd_kernel(
   for (int im = 0; im < kWM; ++im)
 #pragma unroll
     for (int in = 0; in < kWN; ++in) acc[im][in] = f32x16{};
-  gemm_tile(A, B, (uint32_t)k, acc, lds);
+  gemm_tile(A, B, (uint32_t)k, acc, lds0, lds1);
   epilogue(acc, a_amax + row0, kBM, b_amax + brow0, cols, out + (int64_t)row0 * n + col0, n, lsa, lsb);
 }
 
@@ -333,7 +335,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_wgrad_kernel(
     const uint8_t* __restrict__ b_data, const uint8_t* __restrict__ b_scale, const float* __restrict__ b_amax,
     int64_t n, int64_t k, Routing R, ExpertOrder order, bool ordered, uint32_t ntm, uint32_t ntn,
     float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageBytes];
   __shared__ float lsa[kBM], lsb[kBN];
   if (!routing_ok(R)) return;
   const uint32_t t = xcd_supertile_id(), per = ntm * ntn;
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_wgrad_kernel(
   for (int im = 0; im < kWM; ++im)
 #pragma unroll
     for (int in = 0; in < kWN; ++in) acc[im][in] = f32x16{};
-  gemm_tile(A, B, me, acc, lds);
+  gemm_tile(A, B, me, acc, lds0, lds1);
   epilogue(acc, a_amax + (int64_t)e * n + i0, rows_i, b_amax + (int64_t)e * k + j0, rows_j,
            out + (int64_t)e * n * k + i0 * k + j0, k, lsa, lsb);
 }
