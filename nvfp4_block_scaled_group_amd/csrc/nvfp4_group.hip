@@ -228,16 +228,20 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
     const int e = find_expert(R, row0, &rbeg, &rend);
     const uint32_t me = (uint32_t)(rend - rbeg);
 
+    // the line amax loads go first: the line scales are then computed while
+    // the tile's loads are in flight
+    const float a_row = row_data && tid < kTileRows ? row_amax[row0 + tid] : 0.0f;
+    const float a_col = col_data && (uint32_t)tid < ncols ? col_amax[(int64_t)e * k + col_base + tid] : 0.0f;
     uint32_t v[16][4];
     load_tile(x + (int64_t)row0 * k + col_base, ku, vo_x, v);
     bool slow_line = false;
     if (row_data && tid < kTileRows) {
-      const float s = row_amax[row0 + tid] / 2688.0f;
+      const float s = a_row / 2688.0f;
       l_row[tid] = make_float2(s, 1.0f / s);
       slow_line = !(s >= kFastMinLineScale);
     }
     if (col_data) {
-      const float s = (uint32_t)tid < ncols ? col_amax[(int64_t)e * k + col_base + tid] / 2688.0f : 0.0f;
+      const float s = a_col / 2688.0f;
       l_col[tid] = make_float2(s, 1.0f / s);
       slow_line = slow_line || ((uint32_t)tid < ncols && !(s >= kFastMinLineScale));
     }
