@@ -28,10 +28,14 @@
 //    the transposed cast needs no LDS round trip, and 8 neighbouring lanes
 //    write 64 contiguous bytes of a transposed line.
 //  * amax: abs-max on bf16 bit patterns (integer max orders non-negative
-//    floats), reduced across lanes, then one atomic max per row and per
-//    column per tile into zero-initialised outputs (atomic max of the fp32
-//    bit patterns of non-negative values is order independent, so results
-//    are deterministic).
+//    floats), reduced across lanes, then atomic max into zero-initialised
+//    outputs: one per row per 512-column chunk, and one per column each time
+//    a workgroup's run of tiles leaves an (expert, chunk) pair (atomic max of
+//    the fp32 bit patterns of non-negative values is order independent, so
+//    results are deterministic).
+//  * cast: the rowwise data is staged in LDS and written as whole 128-byte
+//    lines, the scales are staged and written one piece per line per tile,
+//    and the transposed data goes out directly (see the kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <float.h>
@@ -276,7 +280,8 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
                                       : block_step(__uint_as_float(b16 << 16), sl.x, sl.y, &m);
           const float mo = __uint_as_float(swap8(__float_as_uint(m)));
           reinterpret_cast<uint8_t*>(&l_rs[16 * rb + ri][0])[wave * 4 + (cg >> 1)] = (uint8_t)S;
-          // bytes lcol/2 .. +3 of row 16*rb + r: dword 8*wave + cg, swizzled
+          // bytes lcol/2 .. +3 of rows 16*rb + i and 16*rb + 8 + i: dword
+          // 8*wave + cg of the row, swizzled
           const float m_lo = odd ? mo : m, m_hi = odd ? m : mo;
           uint32_t packed = 0;
           packed = FP4X2(packed, bf16lo(v[i][0]) * m_lo, bf16hi(v[i][0]) * m_lo, 0);
@@ -410,23 +415,33 @@ __global__ __launch_bounds__(kThreads) void group_quantize_rowwise_kernel(
     if (lane == 0) row_amax[r] = A;
     const float s = A / 2688.0f, ys = 1.0f / s;
     const rsrc_t rd = make_rsrc(row_data + (int64_t)__builtin_amdgcn_readfirstlane(r) * (k / 2));
+    auto encode = [&](auto fast_tag) {
+      constexpr bool kFast = decltype(fast_tag)::value;
 #pragma unroll
-    for (int g = 0; g < NSEG; ++g) {
-      uint32_t b = hmax(pkmax(pkmax(v[g][0] & 0x7FFF7FFFu, v[g][1] & 0x7FFF7FFFu),
-                              pkmax(v[g][2] & 0x7FFF7FFFu, v[g][3] & 0x7FFF7FFFu)));
-      b = max(b, dpp_x1(b));  // the block is lanes 2j, 2j+1
-      float m;
-      const uint32_t S = block_step(__uint_as_float(b << 16), s, ys, &m);
-      uint32_t packed = 0;
-      packed = FP4X2(packed, bf16lo(v[g][0]) * m, bf16hi(v[g][0]) * m, 0);
-      packed = FP4X2(packed, bf16lo(v[g][1]) * m, bf16hi(v[g][1]) * m, 1);
-      packed = FP4X2(packed, bf16lo(v[g][2]) * m, bf16hi(v[g][2]) * m, 2);
-      packed = FP4X2(packed, bf16lo(v[g][3]) * m, bf16hi(v[g][3]) * m, 3);
-      const uint32_t c = (uint32_t)g * 512u + lane * 8u;
-      __builtin_amdgcn_raw_buffer_store_b32(packed, rd, off[g] == kOutOfRange ? kOutOfRange : c / 2u, 0,
-                                            kStoreAux);
-      if (!(lane & 1) && c < ku) row_scale[(int64_t)r * (k / 16) + c / 16] = (uint8_t)S;
-    }
+      for (int g = 0; g < NSEG; ++g) {
+        uint32_t b = hmax(pkmax(pkmax(v[g][0] & 0x7FFF7FFFu, v[g][1] & 0x7FFF7FFFu),
+                                pkmax(v[g][2] & 0x7FFF7FFFu, v[g][3] & 0x7FFF7FFFu)));
+        b = max(b, dpp_x1(b));  // the block is lanes 2j, 2j+1
+        float m;
+        const uint32_t S = kFast ? block_scale_fast(__uint_as_float(b << 16), s, ys, &m)
+                                 : block_scale(__uint_as_float(b << 16), s, &m);
+        uint32_t packed = 0;
+        packed = FP4X2(packed, bf16lo(v[g][0]) * m, bf16hi(v[g][0]) * m, 0);
+        packed = FP4X2(packed, bf16lo(v[g][1]) * m, bf16hi(v[g][1]) * m, 1);
+        packed = FP4X2(packed, bf16lo(v[g][2]) * m, bf16hi(v[g][2]) * m, 2);
+        packed = FP4X2(packed, bf16lo(v[g][3]) * m, bf16hi(v[g][3]) * m, 3);
+        const uint32_t c = (uint32_t)g * 512u + lane * 8u;
+        __builtin_amdgcn_raw_buffer_store_b32(packed, rd, off[g] == kOutOfRange ? kOutOfRange : c / 2u, 0,
+                                              kStoreAux);
+        if (!(lane & 1) && c < ku) row_scale[(int64_t)r * (k / 16) + c / 16] = (uint8_t)S;
+      }
+    };
+    // the row's line scale is the same in every lane: one wave-uniform choice
+    // between the fast block step and the exact one (block_step's rule)
+    if (uni((uint32_t)(s >= kFastMinLineScale)))
+      encode(BoolTag<true>{});
+    else
+      encode(BoolTag<false>{});
   };
 
   uint32_t va[NSEG][4], vb[NSEG][4];
