@@ -79,11 +79,11 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 
 // E4M3FN code of t >= 0 (finite or +inf): nearest, ties to even, saturating
 // at 448 (0x7E).  gfx950's v_cvt_pk_fp8_f32 (OCP E4M3FN) rounds to nearest
-// with ties to even and, checked on the hardware against the plain rule
-// (round the fp32 mantissa to 3 bits and re-bias the exponent by 7 - 127;
-// below 2^-6 the nearest multiple of 2^-9) over every fp32 t in [0, 464),
-// gives the same code; it does not saturate, so t is clamped at 448 first
-// (every t >= 448 then encodes as 0x7E, as the rule says).
+// with ties to even; it does not saturate (t >= 464 gives NaN), so t is
+// clamped at 448 first.  With the clamp it equals the plain rule (round the
+// fp32 mantissa to 3 bits and re-bias the exponent by 7 - 127; below 2^-6
+// the nearest multiple of 2^-9; 0x7E from 448 up) on every fp32 t in
+// [0, +inf], as checked on the hardware by the GPU self-test.
 __device__ __forceinline__ uint32_t e4m3_code(float t) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
