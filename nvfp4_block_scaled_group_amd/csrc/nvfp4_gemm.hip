@@ -262,7 +262,9 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
 }
 
 // out[i, j] = (acc * sa[i]) * sb[j] for i < rows_i, j < rows_j; the line
-// scales of the tile are staged in LDS first.
+// scales of the tile are staged in LDS first.  The fp32 output is written
+// with streaming stores (the weight gradient's [E, N, K] output is 1.9 GB at
+// the expert-share shapes: 1881 -> 1833 us).
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[kWM][kWN], const float* a_amax, uint32_t rows_i,
                                          const float* b_amax, uint32_t rows_j, float* out, int64_t ldo,
                                          float* lsa, float* lsb) {
@@ -284,7 +286,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[kWM][kWN], const fl
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const uint32_t i = wm * (kWM * 32) + im * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (i < rows_i && j < rows_j) out[(int64_t)i * ldo + j] = (acc[im][in][v] * lsa[i]) * sb;
+        if (i < rows_i && j < rows_j)  // streaming store: the output is not read again here
+          __builtin_nontemporal_store((acc[im][in][v] * lsa[i]) * sb, &out[(int64_t)i * ldo + j]);
       }
   }
 }
