@@ -228,7 +228,9 @@ int mxfp4_group_cast_graphsafe(const uint16_t* x, int64_t m_capacity,
  *     out = (acc * (a_amax[r] / 2688)) * (b_amax[e*n + j] / 2688)
  * with acc the fp32 MFMA sum of the exact products value(code)*value(S)
  * (fp16 operands).  For the data gradient pass the columnwise cast of each
- * expert's weight as b.  out: fp32 [sum_m, n], row-major, caller-owned.
+ * expert's weight as b.  Scale bytes are expected to be codes the cast
+ * writes (0x00 .. 0x7E); other bytes give unspecified values (no error is
+ * reported).  out: fp32 [sum_m, n], row-major, caller-owned.
  * k a positive multiple of 128 (<= 2^22), n a positive multiple of 16
  * (<= 2^20); data pointers 16-byte aligned, scale and amax pointers 4-byte
  * aligned; otherwise NVFP4G_EINVAL / NVFP4G_EALIGN and nothing is enqueued. */
