@@ -29,6 +29,8 @@
  *     m = 1 / d               (0 when d == 0, at most FLT_MAX)
  *     code = sign(x*m) << 3 | E2M1(|x*m|)   nearest on {0,.5,1,1.5,2,3,4,6},
  *                                           ties to the even code, saturating
+ * x must be finite: a NaN or infinite element gives unspecified codes and
+ * scales for its lines (no error is reported).
  *
  * Layouts (all row-major, unswizzled; expert e owns rows [r_e, r_e + M_e),
  * M_e a multiple of 128, experts packed in order):
