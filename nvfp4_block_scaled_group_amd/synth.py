@@ -193,6 +193,35 @@ def random_case(seed: int, splits, k: int, dist: str = "normal") -> Workload:
                     True, True, {"seed": seed})
 
 
+def _rowscaled_blocks(rng, sum_m: int, k: int, block_rows: int) -> np.ndarray:
+    """N(0,1) x per-row exp(N(0,1)) as bf16 bits, drawn block_rows rows at a
+    time (bounded host memory for very large buffers)."""
+    x = np.empty((sum_m, k), dtype=np.uint16)
+    for r0 in range(0, sum_m, block_rows):
+        r1 = min(r0 + block_rows, sum_m)
+        v = _normal(rng, (r1 - r0, k)) * np.exp(_normal(rng, (r1 - r0, 1)))
+        x[r0:r1] = f32_to_bf16_bits(np.asarray(v, np.float32))
+    return x
+
+
+def max_rows(seed: int = 6) -> Workload:
+    """The row limit of the C ABI: sum_M = 2^24 rows, K = 16, two experts
+    (one of 2^24 - 2^17 rows, one of 2^17)."""
+    rng = np.random.default_rng(seed)
+    sum_m, k = 1 << 24, 16
+    splits = np.array([sum_m - (1 << 17), 1 << 17], dtype=np.int64)
+    return Workload("max_rows_e2_k16_m16777216", _rowscaled_blocks(rng, sum_m, k, 1 << 20), splits,
+                    True, True, {"seed": seed})
+
+
+def max_k(seed: int = 7) -> Workload:
+    """The column limit of the C ABI: K = 2^22, one expert of 128 rows."""
+    rng = np.random.default_rng(seed)
+    sum_m, k = 128, 1 << 22
+    return Workload("max_k_e1_k4194304_m128", _rowscaled_blocks(rng, sum_m, k, 16),
+                    np.array([sum_m], dtype=np.int64), True, True, {"seed": seed})
+
+
 CONFIGS = {
     "tiny": tiny,
     "outliers": outliers,

@@ -1,0 +1,115 @@
+"""The amax + cast at the size limits of the C ABI, where the kernels' 32-bit
+buffer offsets are largest: 2^24 rows (K = 16, two experts, one of
+2^24 - 2^17 rows) and K = 2^22 columns (128 rows).  Inputs are seeded
+row-scaled normals (synth.max_rows, synth.max_k).  Checked against the oracle
+line by line where it can afford it, and elsewhere by properties that hold at
+any size: the row and column amax equal the maximum of |x| over the line
+(exact, compared on bf16 bit patterns, which order non-negative values), the
+graph-safe call equals the host-split one byte for byte, and the rowwise-only
+request at K = 2^22 equals the rowwise half of the both-directions call.
+"""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_block_scaled_group_amd import binding as B
+from nvfp4_block_scaled_group_amd import synth
+from oracle import oracle as O
+
+from gpu_helpers import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, rowwise=True, columnwise=True):
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    out = B.alloc_outputs(w.sum_m, w.k, w.num_experts, rowwise, columnwise, device=dev)
+    B.nvfp4_group_quantize(x, [int(v) for v in w.splits], **out)
+    torch.cuda.synchronize()
+    return x, out
+
+
+def _abs_bits(x):
+    return (x & np.uint16(0x7FFF)).astype(np.uint16)
+
+
+def _amax_from_bits(b16):
+    return (b16.astype(np.uint32) << 16).view(np.float32)
+
+
+def _check_col_line(w, out, e, c):
+    offs = np.concatenate([[0], np.cumsum(w.splits)]).astype(np.int64)
+    r0, m, k = int(offs[e]), int(w.splits[e]), w.k
+    A = O.col_amax(w.x, c, r0, m)
+    assert out["col_amax"][e * k + c] == A, f"col_amax[{e}, {c}]"
+    d, s = O.cast_col(w.x, c, r0, m, A)
+    d0, s0 = k * r0 // 2 + c * (m // 2), k * r0 // 16 + c * (m // 16)
+    assert np.array_equal(out["col_data"][d0:d0 + m // 2], d), f"col_data expert {e} column {c}"
+    assert np.array_equal(out["col_scale"][s0:s0 + m // 16], s), f"col_scale expert {e} column {c}"
+
+
+def _check_row(w, out, r):
+    A = O.row_amax(w.x, r)
+    assert out["row_amax"][r] == A, f"row_amax[{r}]"
+    d, s = O.cast_row(w.x, r, A)
+    assert np.array_equal(out["row_data"][r], d), f"row_data[{r}]"
+    assert np.array_equal(out["row_scale"][r], s), f"row_scale[{r}]"
+
+
+def test_row_limit_2_to_24_rows():
+    log("generating 2^24 x 16")
+    w = synth.max_rows()
+    log(f"quantize {w.name}")
+    x, dout = _run(w)
+    out = {key: t.cpu().numpy() for key, t in dout.items()}
+    # every row amax: the max of |x| over the row (exact)
+    want = _amax_from_bits(_abs_bits(w.x).max(axis=1))
+    assert np.array_equal(out["row_amax"].view(np.uint32), want.view(np.uint32))
+    # every column line of both experts against the oracle
+    log("column lines vs oracle")
+    for e in range(w.num_experts):
+        for c in range(w.k):
+            _check_col_line(w, out, e, c)
+    # sampled rows, including both ends of each expert
+    rng = np.random.default_rng(61)
+    r1 = int(w.splits[0])
+    rows = [0, 1, r1 - 1, r1, w.sum_m - 1] + rng.integers(0, w.sum_m, 200).tolist()
+    for r in rows:
+        _check_row(w, out, r)
+    # the graph-safe call on the same routing: byte-identical
+    log("graph-safe at 2^24 rows")
+    d_offs = torch.tensor(B.offsets_from_splits([int(v) for v in w.splits]), dtype=torch.int32, device="cuda:0")
+    d_status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    gout = B.alloc_outputs(w.sum_m, w.k, w.num_experts, True, True, device="cuda:0")
+    B.nvfp4_group_quantize_graphsafe(x, w.num_experts, d_offs, d_status, **gout)
+    torch.cuda.synchronize()
+    assert int(d_status.item()) == 0
+    for key in dout:
+        assert torch.equal(gout[key], dout[key]), key
+
+
+def test_column_limit_k_2_to_22():
+    log("generating 128 x 2^22")
+    w = synth.max_k()
+    log(f"quantize {w.name}")
+    x, dout = _run(w)
+    out = {key: t.cpu().numpy() for key, t in dout.items()}
+    # every column amax: the max of |x| over the column (exact)
+    want = _amax_from_bits(_abs_bits(w.x).max(axis=0))
+    assert np.array_equal(out["col_amax"].view(np.uint32), want.view(np.uint32))
+    # every row amax and sampled rows (4M elements each) against the oracle
+    for r in range(w.sum_m):
+        assert out["row_amax"][r] == O.row_amax(w.x, r), f"row_amax[{r}]"
+    for r in (0, 1, 77, w.sum_m - 1):
+        _check_row(w, out, r)
+    # sampled column lines, including the last chunk
+    rng = np.random.default_rng(71)
+    cols = [0, 1, 255, 256, w.k - 256, w.k - 16, w.k - 1] + rng.integers(0, w.k, 200).tolist()
+    for c in cols:
+        _check_col_line(w, out, 0, c)
+    # rowwise-only request (the fused pass does not cover this K: amax + cast)
+    log("rowwise-only at K = 2^22")
+    _, rout = _run(w, rowwise=True, columnwise=False)
+    for key in ("row_amax", "row_data", "row_scale"):
+        assert torch.equal(rout[key], dout[key]), key
