@@ -204,13 +204,13 @@ def _rowscaled_blocks(rng, sum_m: int, k: int, block_rows: int) -> np.ndarray:
     return x
 
 
-def max_rows(seed: int = 6) -> Workload:
-    """The row limit of the C ABI: sum_M = 2^24 rows, K = 16, two experts
-    (one of 2^24 - 2^17 rows, one of 2^17)."""
+def max_rows(seed: int = 6, k: int = 16) -> Workload:
+    """The row limit of the C ABI: sum_M = 2^24 rows, K = 16 (or k), two
+    experts (one of 2^24 - 2^17 rows, one of 2^17)."""
     rng = np.random.default_rng(seed)
-    sum_m, k = 1 << 24, 16
+    sum_m = 1 << 24
     splits = np.array([sum_m - (1 << 17), 1 << 17], dtype=np.int64)
-    return Workload("max_rows_e2_k16_m16777216", _rowscaled_blocks(rng, sum_m, k, 1 << 20), splits,
+    return Workload(f"max_rows_e2_k{k}_m16777216", _rowscaled_blocks(rng, sum_m, k, 1 << 20), splits,
                     True, True, {"seed": seed})
 
 
@@ -220,6 +220,22 @@ def max_k(seed: int = 7) -> Workload:
     sum_m, k = 128, 1 << 22
     return Workload("max_k_e1_k4194304_m128", _rowscaled_blocks(rng, sum_m, k, 16),
                     np.array([sum_m], dtype=np.int64), True, True, {"seed": seed})
+
+
+def random_encoded(seed: int, nbytes_data: int):
+    """Seeded NVFP4-encoded bytes for decode tests: nbytes_data code bytes
+    (every byte value) and nbytes_data / 8 scale bytes (the codes a cast
+    writes, 0x00 .. 0x7E).  Line amax values come from ``random_amax``."""
+    rng = np.random.default_rng(seed)
+    data = rng.integers(0, 256, nbytes_data, dtype=np.uint8)
+    scale = rng.integers(0, 0x7F, nbytes_data // 8, dtype=np.uint8)
+    return data, scale
+
+
+def random_amax(seed: int, lines: int) -> np.ndarray:
+    """Seeded positive line amax values spanning several binades."""
+    rng = np.random.default_rng(seed)
+    return np.exp2(rng.uniform(-8.0, 8.0, lines)).astype(np.float32)
 
 
 CONFIGS = {

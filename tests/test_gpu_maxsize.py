@@ -6,7 +6,10 @@ line by line where it can afford it, and elsewhere by properties that hold at
 any size: the row and column amax equal the maximum of |x| over the line
 (exact, compared on bf16 bit patterns, which order non-negative values), the
 graph-safe call equals the host-split one byte for byte, and the rowwise-only
-request at K = 2^22 equals the rowwise half of the both-directions call.
+request at K = 2^22 equals the rowwise half of the both-directions call.  The
+MXFP4 cast (2^24 rows at K = 32, and K = 2^22) and the dequant (seeded
+encoded bytes at both limits) are checked on sampled lines against the
+oracle the same way.
 """
 import numpy as np
 import pytest
@@ -113,3 +116,65 @@ def test_column_limit_k_2_to_22():
     _, rout = _run(w, rowwise=True, columnwise=False)
     for key in ("row_amax", "row_data", "row_scale"):
         assert torch.equal(rout[key], dout[key]), key
+
+
+@pytest.mark.parametrize("which", ["rows", "k"])
+def test_mxfp4_at_the_limits(which):
+    # 2^24 rows with K = 32 (MXFP4 blocks are 32 wide), or K = 2^22
+    w = synth.max_rows(k=32) if which == "rows" else synth.max_k()
+    log(f"mxfp4 cast {w.name}")
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    mx = B.alloc_mx_outputs(w.sum_m, w.k, device=dev)
+    B.mxfp4_group_cast(x, [int(v) for v in w.splits], **mx)
+    torch.cuda.synchronize()
+    out = {key: t.cpu().numpy() for key, t in mx.items()}
+    f32 = lambda bits: synth.bf16_bits_to_f32(np.ascontiguousarray(bits))
+    rng = np.random.default_rng(81)
+    for r in [0, w.sum_m - 1] + rng.integers(0, w.sum_m, 20).tolist():
+        d, s = O.mx_encode_line(f32(w.x[r]))
+        assert np.array_equal(out["row_data"][r], d) and np.array_equal(out["row_scale"][r], s), f"row {r}"
+    offs = np.concatenate([[0], np.cumsum(w.splits)]).astype(np.int64)
+    cols = list(range(w.k)) if w.k <= 32 else [0, 1, w.k - 1] + rng.integers(0, w.k, 50).tolist()
+    for e in range(w.num_experts):
+        r0, m = int(offs[e]), int(w.splits[e])
+        for c in cols:
+            d, s = O.mx_encode_line(f32(w.x[r0:r0 + m, c]))
+            d0, s0 = w.k * r0 // 2 + c * (m // 2), w.k * r0 // 32 + c * (m // 32)
+            assert np.array_equal(out["col_data"][d0:d0 + m // 2], d), f"col {e}, {c}"
+            assert np.array_equal(out["col_scale"][s0:s0 + m // 32], s), f"col scale {e}, {c}"
+
+
+@pytest.mark.parametrize("rows,k,splits", [(1 << 24, 16, [(1 << 24) - (1 << 17), 1 << 17]),
+                                           (128, 1 << 22, [128])])
+def test_dequant_at_the_limits(rows, k, splits):
+    # seeded encoded inputs (every code byte, valid scale codes) sized at the limits
+    n = rows * k
+    log(f"dequant {rows} x {k}")
+    data, scale = synth.random_encoded(91, n // 2)
+    dev = torch.device("cuda:0")
+    d_data, d_scale = torch.from_numpy(data).to(dev), torch.from_numpy(scale).to(dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(92)
+    # rowwise: lines are rows of k elements
+    ra = synth.random_amax(93, rows)
+    B.nvfp4_group_dequant_rowwise(d_data.view(rows, k // 2), d_scale.view(rows, k // 16),
+                                  torch.from_numpy(ra).to(dev), out.view(rows, k))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(rows, k)
+    for r in [0, rows - 1] + rng.integers(0, rows, 30).tolist():
+        want = O.decode_line(data[r * k // 2:(r + 1) * k // 2], scale[r * k // 16:(r + 1) * k // 16], k, ra[r])
+        assert np.array_equal(got[r].view(np.uint32), want.view(np.uint32)), f"row {r}"
+    # columnwise: per expert k lines of M_e elements
+    ca = synth.random_amax(94, len(splits) * k)
+    B.nvfp4_group_dequant_columnwise(d_data, d_scale, torch.from_numpy(ca).to(dev), splits, k, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    offs = np.concatenate([[0], np.cumsum(splits)]).astype(np.int64)
+    for e, m in enumerate(splits):
+        r0 = int(offs[e])
+        for c in [0, k - 1] + rng.integers(0, k, 10).tolist():
+            base = k * r0 + c * m
+            want = O.decode_line(data[base // 2:(base + m) // 2], scale[base // 16:(base + m) // 16], m,
+                                 ca[e * k + c])
+            assert np.array_equal(got[base:base + m].view(np.uint32), want.view(np.uint32)), f"col {e}, {c}"
