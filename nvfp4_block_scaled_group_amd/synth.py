@@ -238,6 +238,25 @@ def random_amax(seed: int, lines: int) -> np.ndarray:
     return np.exp2(rng.uniform(-8.0, 8.0, lines)).astype(np.float32)
 
 
+def exact_nvfp4_lines(seed: int, lines: int, length: int):
+    """Seeded encoded lines whose dot products are exact in fp32 for lengths
+    up to 2^22: E2M1 codes of 0, +-0.5, +-1 (0, 1, 2, 9, 10), every block
+    scale 1.0 (E4M3 0x38) and line amax 2688 (line factor 1), so every
+    partial sum is a multiple of 0.25 of magnitude <= 2^22.  Returns
+    (data [lines, length/2], scale [lines, length/16], amax [lines])."""
+    rng = np.random.default_rng(seed)
+    codes = np.array([0, 1, 2, 9, 10], dtype=np.uint8)
+    data = np.empty((lines, length // 2), dtype=np.uint8)
+    step = max(1, (1 << 24) // length)  # lines per draw
+    for i0 in range(0, lines, step):
+        i1 = min(i0 + step, lines)
+        nib = codes[rng.integers(0, codes.size, (i1 - i0, length))]
+        data[i0:i1] = nib[:, 0::2] | (nib[:, 1::2] << 4)
+    scale = np.full((lines, length // 16), 0x38, dtype=np.uint8)
+    amax = np.full(lines, 2688.0, dtype=np.float32)
+    return data, scale, amax
+
+
 CONFIGS = {
     "tiny": tiny,
     "outliers": outliers,

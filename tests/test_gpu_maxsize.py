@@ -9,7 +9,10 @@ graph-safe call equals the host-split one byte for byte, and the rowwise-only
 request at K = 2^22 equals the rowwise half of the both-directions call.  The
 MXFP4 cast (2^24 rows at K = 32, and K = 2^22) and the dequant (seeded
 encoded bytes at both limits) are checked on sampled lines against the
-oracle the same way.
+oracle the same way.  The grouped GEMM is run at its limits (contraction
+k = 2^22, n = 2^20, 2^22 rows per expert in the weight gradient) on operands
+whose fp32 sums are exact (element values 0, +-0.5, +-1, unit scales), so its
+outputs must equal the oracle's float64 dot products exactly.
 """
 import numpy as np
 import pytest
@@ -178,3 +181,57 @@ def test_dequant_at_the_limits(rows, k, splits):
             want = O.decode_line(data[base // 2:(base + m) // 2], scale[base // 16:(base + m) // 16], m,
                                  ca[e * k + c])
             assert np.array_equal(got[base:base + m].view(np.uint32), want.view(np.uint32)), f"col {e}, {c}"
+
+
+def _values(data, scale, length):
+    return O.block_values(data, scale, length)  # value(code) * value(S), exact in float64
+
+
+def test_gemm_forward_at_k_2_to_22_exact():
+    # sums of 2^22 products of 0, +-0.5, +-1: exact in fp32, so out == the
+    # oracle's float64 product exactly
+    k, n, rows = 1 << 22, 16, 128
+    log("gemm forward k = 2^22")
+    ad, as_, aa = synth.exact_nvfp4_lines(101, rows, k)
+    bd, bs, ba = synth.exact_nvfp4_lines(102, n, k)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    out = torch.empty((rows, n), dtype=torch.float32, device="cuda:0")
+    B.nvfp4_group_gemm(dev(ad), dev(as_), dev(aa), dev(bd.reshape(1, n, -1)), dev(bs.reshape(1, n, -1)), dev(ba),
+                       [rows], out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    vb = _values(bd, bs, k)
+    for r in (0, 1, 64, rows - 1):
+        want = _values(ad[r:r + 1], as_[r:r + 1], k) @ vb.T
+        assert np.array_equal(got[r:r + 1], want), f"row {r}"
+
+
+def test_gemm_forward_at_n_2_to_20_exact():
+    k, n, rows = 128, 1 << 20, 128
+    log("gemm forward n = 2^20")
+    ad, as_, aa = synth.exact_nvfp4_lines(103, rows, k)
+    bd, bs, ba = synth.exact_nvfp4_lines(104, n, k)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    out = torch.empty((rows, n), dtype=torch.float32, device="cuda:0")
+    B.nvfp4_group_gemm(dev(ad), dev(as_), dev(aa), dev(bd.reshape(1, n, -1)), dev(bs.reshape(1, n, -1)), dev(ba),
+                       [rows], out)
+    torch.cuda.synchronize()
+    cols = np.array([0, 1, 255, 256, n - 256, n - 1] + np.random.default_rng(105).integers(0, n, 64).tolist())
+    got = out[:, torch.from_numpy(cols).to("cuda:0")].cpu().numpy().astype(np.float64)
+    want = _values(ad, as_, k) @ _values(bd[cols], bs[cols], k).T
+    assert np.array_equal(got, want)
+
+
+def test_gemm_wgrad_at_2_to_22_rows_exact():
+    # one expert of 2^22 rows (the weight gradient's limit); every output
+    m, n, k = 1 << 22, 16, 16
+    log("gemm weight gradient, 2^22 rows")
+    yd, ys, ya = synth.exact_nvfp4_lines(106, n, m)   # dY^T lines [n, m]
+    xd, xs, xa = synth.exact_nvfp4_lines(107, k, m)   # X^T lines [k, m]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).to("cuda:0")
+    out = torch.empty((1, n, k), dtype=torch.float32, device="cuda:0")
+    B.nvfp4_group_gemm_wgrad(dev(yd), dev(ys), dev(ya), dev(xd), dev(xs), dev(xa), [m], n, k, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0].astype(np.float64)
+    want = _values(yd, ys, m) @ _values(xd, xs, m).T
+    assert np.array_equal(got, want)
