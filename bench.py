@@ -28,7 +28,9 @@ the grouped MXFP4 cast of the same input (one read of x, both MXFP4 outputs
 written), the rowwise / columnwise NVFP4 dequant of the step's outputs
 (codes, scales and line amax read once, fp32 written), and the row-scaled
 grouped GEMM (forward and weight gradient, MFMA-bound, TFLOP/s against the
-fp16 MFMA peak), each timed with HIP events over repeated launches.
+fp16 MFMA peak), each timed with HIP events over repeated launches; beside
+the GEMM, torch.matmul (hipBLASLt) in fp16 on operands of the same shapes,
+for context.
 """
 from __future__ import annotations
 
@@ -417,6 +419,45 @@ def gemm_rows(B, torch, timed, out, splits, E: int, k: int, m: int) -> dict:
                                                 n, k, dw))
     res["nvfp4_group_gemm_wgrad"] = entry("gemm_wgrad_kernel", ms)
     del dy, dw
+    res["library_fp16"] = library_gemm_rows(torch, timed, splits, n, k, m, dev)
+    return res
+
+
+def library_gemm_rows(torch, timed, splits, n: int, k: int, m: int, dev) -> dict:
+    """Context for the grouped GEMM's rate: torch.matmul (hipBLASLt) in fp16 on
+    operands of the same shapes, already decoded (no FP4 decode, fp16 output,
+    half the output bytes of the fp32 kernels).  Per expert as a loop of
+    GEMMs (what a grouped product costs through the library), and the forward
+    as one dense GEMM over all rows with one weight (an upper bound: no
+    grouping).  Not part of the path."""
+    print("[bench] library fp16 GEMMs (context)", file=sys.stderr, flush=True)
+    flops = 2.0 * m * n * k
+    offs = np.concatenate([[0], np.cumsum(splits)]).tolist()
+    live = [(e, offs[e], offs[e + 1]) for e in range(len(splits)) if splits[e]]
+    h = torch.float16
+    a = torch.randn(m, k, dtype=h, device=dev)
+    wts = torch.randn(len(splits), n, k, dtype=h, device=dev)
+    dyt = torch.randn(n, m, dtype=h, device=dev)
+
+    def fwd_loop():
+        for e, r0, r1 in live:
+            torch.matmul(a[r0:r1], wts[e].t())
+
+    def wgrad_loop():
+        for _, r0, r1 in live:
+            torch.matmul(dyt[:, r0:r1], a[r0:r1])
+
+    def rate(ms):
+        return {"avg_us": round(ms * 1e3, 2), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1)}
+
+    res = {"grouped_fwd_loop": rate(timed(fwd_loop))}
+    if hasattr(torch, "_grouped_mm"):  # torch's grouped GEMM (offsets = inclusive row ends)
+        ends = torch.tensor(offs[1:], dtype=torch.int32, device=dev)
+        res["grouped_fwd_torch_grouped_mm"] = rate(timed(lambda: torch._grouped_mm(a, wts.transpose(-2, -1),
+                                                                                   offs=ends)))
+    res["dense_fwd_one_gemm"] = rate(timed(lambda: torch.matmul(a, wts[0].t())))
+    res["grouped_wgrad_loop"] = rate(timed(wgrad_loop))
+    del a, wts, dyt
     return res
 
 
