@@ -30,9 +30,13 @@
 //    accumulators per lane), two work-groups per CU so one's barrier and
 //    LDS phase overlaps the other's MFMAs; the contraction advances 128
 //    elements per step.
-//  * LDS holds the raw step: FP4 bytes and E4M3 scale bytes of the A and B
-//    lines (double-buffered; the next step is copied by direct global -> LDS
-//    loads while the current one is multiplied).  Each wave decodes its own fragments
+//  * LDS holds the raw FP4 bytes of the step's A and B lines (double-buffered;
+//    the next step is copied by direct global -> LDS loads while the current
+//    one is multiplied) and, apart, the E4M3 scale bytes of four steps at a
+//    time (32 bytes per line, double-buffered): a copy request costs about
+//    the same whether it moves 4 or 16 bytes per lane, and the per-step
+//    scale copies (8 bytes per line) were half of all requests for a ninth
+//    of the bytes.  Each wave decodes its own fragments
 //    right before the MFMAs: v_cvt_scalef32_pk_f16_fp4 with unit scale gives
 //    the exact E2M1 values two at a time, one packed fp16 multiply applies
 //    value(S) (converted once per block pair by v_cvt_scalef32_pk_f16_fp8).
@@ -100,18 +104,25 @@ __device__ __forceinline__ void grouped_tile(uint32_t t, uint32_t ntm, uint32_t 
   *tn = uni(in / gm);
 }
 
-// LDS stage: the raw FP4 bytes and E4M3 scale bytes of one contraction step,
-// [line][64 bytes] codes and [line][8 bytes] scales for A, then for B.
+// LDS stage: the raw FP4 bytes of one contraction step, [line][64 bytes] for
+// A, then for B.
 constexpr uint32_t kRowBytes = kBK / 2, kRowScales = kBK / 16;
-constexpr uint32_t kStA = 0, kStB = kBM * kRowBytes, kStAS = kStB + kBN * kRowBytes,
-                   kStBS = kStAS + kBM * kRowScales;
-constexpr uint32_t kStageBytes = kStBS + kBN * kRowScales;  // 27 KB
-// copies per thread per stage (direct global -> LDS loads): 16-byte code
-// granules of A and B, 4-byte scale words of A and B
+constexpr uint32_t kStA = 0, kStB = kBM * kRowBytes;
+constexpr uint32_t kStageBytes = kStB + kBN * kRowBytes;  // 24 KB
+// Scale block: the E4M3 scale bytes of kScSteps consecutive steps, 32 bytes
+// per line ([line][32] for A, then for B), double-buffered apart from the
+// code stages.  Block b holds steps 4b .. 4b+3; a line's piece of the last
+// block may run past the line's scales when the step count is not a multiple
+// of 4: those bytes are the next line's (or read as zero past the operand,
+// buffer loads being range-checked per dword) and are never used.
+constexpr uint32_t kScSteps = 4, kScLine = kScSteps * kRowScales;
+constexpr uint32_t kScA = 0, kScB = kBM * kScLine, kScBlockBytes = kScB + kBN * kScLine;  // 12 KB
+// copies per thread (direct global -> LDS loads, 16 bytes each): code
+// granules of A and B per stage, scale halves of A and B per scale block
 constexpr int kCpA = kBM * kRowBytes / 16 / kThreads, kCpB = kBN * kRowBytes / 16 / kThreads;
-constexpr int kCpAS = kBM * kRowScales / 4 / kThreads, kCpBS = kBN * kRowScales / 4 / kThreads;
+constexpr int kCpAS = kBM * kScLine / 16 / kThreads, kCpBS = kBN * kScLine / 16 / kThreads;
 static_assert(kCpA * 16 * kThreads == kBM * kRowBytes && kCpB * 16 * kThreads == kBN * kRowBytes &&
-              kCpAS * 4 * kThreads == kBM * kRowScales && kCpBS * 4 * kThreads == kBN * kRowScales,
+              kCpAS * 16 * kThreads == kBM * kScLine && kCpBS * 16 * kThreads == kBN * kScLine,
               "every thread issues the same copies");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -164,9 +175,14 @@ __device__ __forceinline__ h8_t decode8(uint32_t w, _Float16 S) {
 // flight.  The loop is unrolled by two so that every copy and every read
 // names its stage array: the compiler can then tell that a read of one stage
 // need not wait for copies into the other (with one array and a computed
-// offset it makes every LDS read wait for every copy in flight).
+// offset it makes every LDS read wait for every copy in flight).  The scale
+// blocks share one array, so each step reads its scales before it issues
+// any copy: no copy into that array is then in flight (the step's wait has
+// drained them), and the read of block b and the copy of block b + 1 (issued
+// by the last step of block b, into the other half) never overlap.
 __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTile& B, uint32_t L,
-                                          f32x16 (&acc)[kWM][kWN], uint8_t* lds0, uint8_t* lds1) {
+                                          f32x16 (&acc)[kWM][kWN], uint8_t* lds0, uint8_t* lds1,
+                                          uint8_t* lsc) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // every descriptor field is work-group uniform: keep them in scalar registers
   const uint32_t dpitch = uni(L / 2), spitch = uni(L / 16);
@@ -180,10 +196,10 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
   const uint32_t nk = L / kBK;
   if (nk == 0) return;
 
-  // Copy step ks into stage st.  Copy c of a thread moves granule
-  // g = c * kThreads + tid; a wave's lanes land contiguously in LDS.
+  // Copy the codes of step ks into a stage.  Copy c of a thread moves
+  // granule g = c * kThreads + tid; a wave's lanes land contiguously in LDS.
   auto issue = [&](uint32_t ks, uint8_t* base) {
-    const uint32_t sd = ks * kRowBytes, ss = ks * kRowScales;
+    const uint32_t sd = ks * kRowBytes;
 #pragma unroll
     for (int c = 0; c < kCpA; ++c) {
       const uint32_t g = c * kThreads + tid;  // LDS slot g % 4 of line g / 4
@@ -196,17 +212,22 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bd, (lds_ptr_t)(base + kStB + 16 * (c * kThreads + wave * 64)), 16,
                                                (g >> 2) * dpitch + 16 * swz(g >> 2, g & 3), sd, 0, 0);
     }
+  };
+  // Copy the scales of steps kScSteps * blk .. + kScSteps - 1 into a scale
+  // block: lane g moves 16-byte half g % 2 of line g / 2's 32-byte piece.
+  auto issue_scales = [&](uint32_t blk, uint8_t* sbase) {
+    const uint32_t so = blk * kScLine;
 #pragma unroll
     for (int c = 0; c < kCpAS; ++c) {
-      const uint32_t g = c * kThreads + tid;  // line g / 2, half g % 2
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(as, (lds_ptr_t)(base + kStAS + 4 * (c * kThreads + wave * 64)), 4,
-                                               (g >> 1) * spitch + 4 * (g & 1), ss, 0, 0);
+      const uint32_t g = c * kThreads + tid;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(as, (lds_ptr_t)(sbase + kScA + 16 * (c * kThreads + wave * 64)), 16,
+                                               (g >> 1) * spitch + 16 * (g & 1), so, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < kCpBS; ++c) {
       const uint32_t g = c * kThreads + tid;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs, (lds_ptr_t)(base + kStBS + 4 * (c * kThreads + wave * 64)), 4,
-                                               (g >> 1) * spitch + 4 * (g & 1), ss, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs, (lds_ptr_t)(sbase + kScB + 16 * (c * kThreads + wave * 64)), 16,
+                                               (g >> 1) * spitch + 16 * (g & 1), so, 0, 0);
     }
   };
 
@@ -214,26 +235,40 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
   auto step = [&](uint32_t ks, const uint8_t* base, uint8_t* next) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of step ks
     __syncthreads();
-    if (ks + 1 < nk) issue(ks + 1, next);
-    u32x4 wa[kWM][2], wb[kWN][2];
+    // scales first (see above), two E4M3 codes -> fp16 pairs per line
     h2_t sa[kWM][2], sb[kWN][2];
+    const uint8_t* scb = lsc + ((ks / kScSteps) & 1) * kScBlockBytes + kRowScales * (ks % kScSteps) + 4 * h;
 #pragma unroll
     for (int im = 0; im < kWM; ++im) {
       const uint32_t line = wm * (kWM * 32) + im * 32 + (lane & 31);
-      wa[im][0] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 16 * swz(line, 2 * h));
-      wa[im][1] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 16 * swz(line, 2 * h + 1));
-      const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + kStAS + kRowScales * line + 4 * h);
+      const uint32_t sc = *reinterpret_cast<const uint32_t*>(scb + kScA + kScLine * line);
       sa[im][0] = scales_h2(sc & 0xFFFFu);
       sa[im][1] = scales_h2(sc >> 16);
     }
 #pragma unroll
     for (int in = 0; in < kWN; ++in) {
       const uint32_t line = wn * (kWN * 32) + in * 32 + (lane & 31);
-      wb[in][0] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 16 * swz(line, 2 * h));
-      wb[in][1] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 16 * swz(line, 2 * h + 1));
-      const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + kStBS + kRowScales * line + 4 * h);
+      const uint32_t sc = *reinterpret_cast<const uint32_t*>(scb + kScB + kScLine * line);
       sb[in][0] = scales_h2(sc & 0xFFFFu);
       sb[in][1] = scales_h2(sc >> 16);
+    }
+    if (ks + 1 < nk) {
+      issue(ks + 1, next);
+      const uint32_t nb = (ks + 1) / kScSteps;
+      if ((ks + 1) % kScSteps == 0) issue_scales(nb, lsc + (nb & 1) * kScBlockBytes);
+    }
+    u32x4 wa[kWM][2], wb[kWN][2];
+#pragma unroll
+    for (int im = 0; im < kWM; ++im) {
+      const uint32_t line = wm * (kWM * 32) + im * 32 + (lane & 31);
+      wa[im][0] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 16 * swz(line, 2 * h));
+      wa[im][1] = *reinterpret_cast<const u32x4*>(base + kStA + kRowBytes * line + 16 * swz(line, 2 * h + 1));
+    }
+#pragma unroll
+    for (int in = 0; in < kWN; ++in) {
+      const uint32_t line = wn * (kWN * 32) + in * 32 + (lane & 31);
+      wb[in][0] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 16 * swz(line, 2 * h));
+      wb[in][1] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 16 * swz(line, 2 * h + 1));
     }
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
@@ -250,6 +285,7 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
     }
   };
   issue(0, lds0);
+  issue_scales(0, lsc);
 #pragma unroll 1
   for (uint32_t ks = 0; ks < nk; ks += 2) {
     step(ks, lds0, lds1);
@@ -300,6 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fwd_kernel(
     int64_t n, int64_t k, Routing R, uint32_t ntm, uint32_t ntn, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[2 * kScBlockBytes];
   __shared__ float lsa[kBM], lsb[kBN];
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
@@ -319,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fwd_kernel(
   for (int im = 0; im < kWM; ++im)
 #pragma unroll
     for (int in = 0; in < kWN; ++in) acc[im][in] = f32x16{};
-  gemm_tile(A, B, (uint32_t)k, acc, lds0, lds1);
+  gemm_tile(A, B, (uint32_t)k, acc, lds0, lds1, lsc);
   epilogue(acc, a_amax + row0, kBM, b_amax + brow0, cols, out + (int64_t)row0 * n + col0, n, lsa, lsb);
 }
 
@@ -340,6 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_wgrad_kernel(
     float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[2 * kScBlockBytes];
   __shared__ float lsa[kBM], lsb[kBN];
   if (!routing_ok(R)) return;
   const uint32_t t = xcd_supertile_id(), per = ntm * ntn;
@@ -359,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_wgrad_kernel(
   for (int im = 0; im < kWM; ++im)
 #pragma unroll
     for (int in = 0; in < kWN; ++in) acc[im][in] = f32x16{};
-  gemm_tile(A, B, me, acc, lds0, lds1);
+  gemm_tile(A, B, me, acc, lds0, lds1, lsc);
   epilogue(acc, a_amax + (int64_t)e * n + i0, rows_i, b_amax + (int64_t)e * k + j0, rows_j,
            out + (int64_t)e * n * k + i0 * k + j0, k, lsa, lsb);
 }
