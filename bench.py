@@ -20,8 +20,10 @@ vectors written once and read once, and both outputs written once.
 
 ``flushed_step`` times the same steps with a 512 MB read before each
 (outside the events), so that the 256 MB memory-side cache holds nothing of
-the step's data; ``cpu_baseline`` is the CPU oracle on a bounded sample,
-timed before the process touches the GPU.
+the step's data; ``hbm_ceiling`` times a plain 1 GiB device copy in the same
+process, the practical rate of a stream of reads and writes; ``cpu_baseline``
+is the CPU oracle on a bounded sample, timed before the process touches the
+GPU.
 
 On workloads with both directions the JSON line also carries ``next_rows``:
 the grouped MXFP4 cast of the same input (one read of x, both MXFP4 outputs
@@ -320,6 +322,8 @@ def main():
                                   "unflushed_event_ms_per_step": round(first_ms + second_ms, 4)}
         del flush
 
+    result["hbm_ceiling"] = copy_ceiling(torch, tev, dev)
+
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -338,6 +342,28 @@ def main():
         result["cpu_baseline"] = cpu
     tev.close()
     print(json.dumps(result), flush=True)
+
+
+def copy_ceiling(torch, tev, dev, nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """Context for roofline.frac: a plain device-to-device copy of 1 GiB on
+    the same GPU in the same process (bytes read + written over its time,
+    HIP events on the same stream), the rate a stream that mixes reads and
+    writes reaches on this memory system."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    evs = [(tev.new(), tev.new()) for _ in range(reps)]
+    for e0, e1 in evs:
+        tev.record(e0)
+        dst.copy_(src)
+        tev.record(e1)
+    torch.cuda.synchronize()
+    ms = float(np.mean([tev.elapsed_ms(a, b) for a, b in evs]))
+    del src, dst
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"kind": "device copy, 1 GiB read + 1 GiB written", "avg_us": round(ms * 1e3, 2),
+            "GBps": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def next_rows(B, torch, tev, x, splits, out, E: int, k: int, m: int, reps: int) -> dict:
