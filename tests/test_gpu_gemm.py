@@ -91,6 +91,8 @@ def _weights(rng, E, n, k, dist="normal"):
     ([384, 128], 48, 128, "outliers", 82),              # n below one column tile
     ([128] * 6, 512, 128, "normal", 83),                # a single contraction step
     ([1024, 0, 512, 2560], 320, 2048, "rowscale", 84),  # several row-tile groups, long contraction
+    ([256, 128], 96, 384, "normal", 85),                # 3 steps: the first scale block partial
+    ([128, 384, 0], 160, 896, "outliers", 86),          # 7 steps: the second scale block partial
 ])
 def test_fwd_matches_oracle(splits, n, k, dist, seed):
     w = synth.random_case(seed, splits, k, dist)
