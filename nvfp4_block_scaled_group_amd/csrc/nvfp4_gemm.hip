@@ -33,13 +33,13 @@
 //  * LDS holds the raw FP4 bytes of the step's A and B lines (double-buffered;
 //    the next step is copied by direct global -> LDS loads while the current
 //    one is multiplied) and, apart, the E4M3 scale bytes of four steps at a
-//    time (32 bytes per line, double-buffered): a copy request costs about
-//    the same whether it moves 4 or 16 bytes per lane, and the per-step
-//    scale copies (8 bytes per line) were half of all requests for a ninth
-//    of the bytes.  Each wave decodes its own fragments
-//    right before the MFMAs: v_cvt_scalef32_pk_f16_fp4 with unit scale gives
-//    the exact E2M1 values two at a time, one packed fp16 multiply applies
-//    value(S) (converted once per block pair by v_cvt_scalef32_pk_f16_fp8).
+//    time (32 bytes per line, 16 per lane, double-buffered): copied per step
+//    (8 bytes per line, 4 per lane) the scales took a third of the copy
+//    instructions for a ninth of the bytes.  Each wave decodes its own
+//    fragments right before the MFMAs: v_cvt_scalef32_pk_f16_fp4 with unit
+//    scale gives the exact E2M1 values two at a time, one packed fp16
+//    multiply applies value(S) (converted once per block pair by
+//    v_cvt_scalef32_pk_f16_fp8).
 //  * Global loads are buffer loads: lines beyond an operand read as zero.
 //    The 16-byte granules of a line are XOR-swizzled in LDS so that a
 //    fragment read (32 consecutive lines, same granule) spreads over the
