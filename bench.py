@@ -223,14 +223,17 @@ def main():
     nbytes = algorithmic_bytes(m, k, E, w.rowwise, w.columnwise)
 
     fused = w.rowwise and not w.columnwise
+    # small inputs with a columnwise output: the library's one-launch path
+    small = w.columnwise and max(splits) * k <= B.SMALL_MAX_EXPERT_ELEMS and k <= B.SMALL_MAX_K
 
     tev = TimingEvents(torch)
 
     def step(ev=None):
         if ev is not None:
             tev.record(ev[0])
-        if fused:
-            # rowwise only: one pass (row amax and cast together)
+        if fused or small:
+            # rowwise only: one pass (row amax and cast together); small
+            # inputs: one launch, one work-group per expert
             B.nvfp4_group_quantize(x, splits, **out)
             if ev is not None:
                 tev.record(ev[1])
@@ -263,8 +266,10 @@ def main():
     second_ms = float(np.mean([tev.elapsed_ms(e[1], e[2]) for e in events]))
     ms_per_step = wall * 1e3 / args.steps
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    if fused:
-        dom_name, dom_ms, dom_bytes = "group_quantize_rowwise_kernel", first_ms, nbytes["fused_kernel"]
+    if fused or small:
+        dom_name, dom_ms = ("group_quantize_rowwise_kernel", first_ms) if fused else \
+            ("group_quantize_small_kernel", first_ms)
+        dom_bytes = nbytes["fused_kernel"] if fused else nbytes["step"]
         kernels = {dom_name: {"avg_us": round(dom_ms * 1e3, 2), "GBps": round(dom_bytes / dom_ms / 1e6, 2)}}
     else:
         dom_name, dom_ms, dom_bytes = "group_cast_kernel", second_ms, nbytes["cast_kernel"]
@@ -289,6 +294,7 @@ def main():
                    "directions": "+".join(d for d, on in (("rowwise", w.rowwise), ("columnwise", w.columnwise))
                                           if on),
                    "entry": ("nvfp4_group_quantize (host splits, fused rowwise pass)" if fused
+                             else "nvfp4_group_quantize (host splits, one launch for a small input)" if small
                              else "nvfp4_group_amax + nvfp4_group_cast (host splits)"),
                    "algorithmic_bytes_per_step": nbytes["step"],
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},

@@ -133,7 +133,15 @@ int nvfp4_group_cast_graphsafe(const uint16_t* x, int64_t m_capacity, int64_t k,
  * Description, enqueued back to back).  When no columnwise output is
  * requested the rowwise amax and cast run as one fused pass over x, the
  * one-pass-per-row form of "Implement per-token NVFP4 fprop recipe",
- * Important Files Changed; row_amax is still written. */
+ * Important Files Changed; row_amax is still written.  When a columnwise
+ * output is requested and every expert is small -- the largest expert's
+ * rows times k (m_capacity * k for the graph-safe form, where any expert
+ * may hold all rows) at most NVFP4G_SMALL_MAX_EXPERT_ELEMS, and k at most
+ * NVFP4G_SMALL_MAX_K -- the whole path runs as one launch with one
+ * work-group per expert, where the general path's three launches would
+ * cost more than the work.  Every path writes the same bytes. */
+#define NVFP4G_SMALL_MAX_EXPERT_ELEMS (1 << 16)
+#define NVFP4G_SMALL_MAX_K 512  /* = NVFP4G_SMALL_MAX_EXPERT_ELEMS / 128: an expert has 128 rows or none */
 int nvfp4_group_quantize(const uint16_t* x, int64_t sum_m, int64_t k,
                          int32_t num_experts, const int64_t* h_splits,
                          float* row_amax, float* col_amax, uint8_t* row_data,

@@ -29,6 +29,11 @@ NVFP4G_DEV_NONMONO = 2
 NVFP4G_DEV_OVERFLOW = 4
 MAX_EXPERTS_HOST = 512
 MAX_EXPERTS_DEVICE = 4096
+# nvfp4_group_quantize{,_graphsafe} with a columnwise output runs as one
+# launch when every expert's rows * k <= SMALL_MAX_EXPERT_ELEMS (the
+# capacity's for device routing) and k <= SMALL_MAX_K
+SMALL_MAX_EXPERT_ELEMS = 1 << 16
+SMALL_MAX_K = 512
 
 EXPORTS = (
     "nvfp4_group_amax", "nvfp4_group_cast", "nvfp4_group_amax_graphsafe",

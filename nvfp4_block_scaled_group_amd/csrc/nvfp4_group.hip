@@ -40,6 +40,8 @@
 #include <stdint.h>
 #include <float.h>
 
+#include <algorithm>
+
 #include "../../include/nvfp4_group.h"
 #include "nvfp4_numerics.hpp"
 #include "nvfp4_common.hpp"
@@ -459,6 +461,156 @@ __global__ __launch_bounds__(kThreads) void group_quantize_rowwise_kernel(
   }
 }
 
+// Small inputs in one launch.  When every expert holds at most
+// kSmallMaxExpertElems elements (K <= kSmallMaxK follows, an expert having
+// 128 rows or none), the general path's three launches (zero-fill, amax,
+// cast; ~6 us each, mostly launch latency) cost more than the work.  One
+// workgroup per expert runs the whole path: it copies the expert's rows (one
+// contiguous slice of x, at most 128 KB) into LDS with every load in flight
+// at once, takes the row and column amax there (each written once, so with
+// no zero-fill and no atomics), then the rowwise and columnwise block steps
+// from LDS -- the cast kernel's line scales, block step and FP4 converts, so
+// the bytes are the same.
+constexpr int64_t kSmallMaxExpertElems = NVFP4G_SMALL_MAX_EXPERT_ELEMS;
+constexpr int64_t kSmallMaxK = NVFP4G_SMALL_MAX_K;
+static_assert(kSmallMaxK * 128 == kSmallMaxExpertElems, "K limit = elements of a 128-row expert");
+constexpr int kSmallThreads = 1024;                                // 16 waves
+constexpr int kSmallSplit = 8;  // workgroups per expert: each takes the amax, and 1/8 of the blocks
+constexpr int kSmallMaxRows = (int)(kSmallMaxExpertElems / 16);  // K >= 16
+constexpr int kSmallLoads = (int)(kSmallMaxExpertElems / 8 / kSmallThreads);  // 16-byte loads per thread
+
+__global__ __launch_bounds__(kSmallThreads) void group_quantize_small_kernel(
+    const uint16_t* __restrict__ x, int64_t k, Routing R, float* __restrict__ row_amax,
+    float* __restrict__ col_amax, uint8_t* __restrict__ row_data, uint8_t* __restrict__ row_scale,
+    uint8_t* __restrict__ col_data, uint8_t* __restrict__ col_scale) {
+  __shared__ u32x4 l_x[kSmallMaxExpertElems / 8];       // the expert's rows, row-major bf16
+  __shared__ uint16_t l_bm[kSmallMaxExpertElems / 16];  // amax of each rowwise 16-block (bf16 bits)
+  __shared__ uint16_t l_ra[kSmallMaxRows];              // row amax (bf16 bits)
+  __shared__ uint32_t l_cp[kSmallThreads];              // column maxima: partial, then final pairs
+  if (!routing_ok(R)) return;
+  const int e = blockIdx.x / kSmallSplit, g = blockIdx.x % kSmallSplit;
+  const int32_t rend = route_end(R, e), rbeg = e ? route_end(R, e - 1) : 0;
+  const uint32_t me = (uint32_t)(rend - rbeg);
+  const int tid = threadIdx.x;
+  const bool writer = g == 0;  // the one workgroup of the expert that writes its amax
+  const uint32_t ku = (uint32_t)k, kp = ku / 2, kq = ku / 8;  // bf16 pairs, 16-byte pieces per row
+  const uint16_t* lx16 = reinterpret_cast<const uint16_t*>(l_x);
+  const uint32_t* lx32 = reinterpret_cast<const uint32_t*>(l_x);
+
+  // the expert's slice: me * k contiguous bf16, all loads issued before any store
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)rbeg * k);
+    const uint32_t n = me * kq;
+    u32x4 v[kSmallLoads];
+#pragma unroll
+    for (int u = 0; u < kSmallLoads; ++u) {
+      const uint32_t i = tid + u * kSmallThreads;
+      v[u] = i < n ? src[i] : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kSmallLoads; ++u) {
+      const uint32_t i = tid + u * kSmallThreads;
+      if (i < n) l_x[i] = v[u];
+    }
+  }
+  __syncthreads();
+
+  // the amax of every rowwise 16-block (magnitude bits: bf16 magnitudes
+  // order as their bit patterns)
+  const uint32_t nb = ku / 16;
+  for (uint32_t q = tid; q < me * nb; q += kSmallThreads) {
+    const u32x4 q0 = l_x[2 * q], q1 = l_x[2 * q + 1];
+    l_bm[q] = (uint16_t)hmax(pkmax(pkmax(pkmax(q0.x & 0x7FFF7FFFu, q0.y & 0x7FFF7FFFu),
+                                         pkmax(q0.z & 0x7FFF7FFFu, q0.w & 0x7FFF7FFFu)),
+                                   pkmax(pkmax(q1.x & 0x7FFF7FFFu, q1.y & 0x7FFF7FFFu),
+                                         pkmax(q1.z & 0x7FFF7FFFu, q1.w & 0x7FFF7FFFu))));
+  }
+  // column amax: thread t takes column pair t % kp over rows t / kp + nseg * j
+  const uint32_t nseg = kSmallThreads / kp;
+  {
+    uint32_t m = 0;
+    if ((uint32_t)tid < nseg * kp) {
+      const uint32_t p = tid % kp;
+      for (uint32_t r = tid / kp; r < me; r += nseg) m = pkmax(m, lx32[r * kp + p] & 0x7FFF7FFFu);
+    }
+    l_cp[tid] = m;
+  }
+  __syncthreads();
+  // row amax: the max of the row's block maxima, a thread per row
+  for (uint32_t r = tid; r < me; r += kSmallThreads) {
+    uint32_t m = 0;
+    for (uint32_t b = 0; b < nb; ++b) m = max(m, (uint32_t)l_bm[r * nb + b]);
+    l_ra[r] = (uint16_t)m;
+    if (row_amax && writer) row_amax[rbeg + r] = __uint_as_float(m << 16);
+  }
+  uint32_t cpair = 0;
+  if ((uint32_t)tid < kp) {
+    for (uint32_t g = 0; g < nseg; ++g) cpair = pkmax(cpair, l_cp[g * kp + tid]);
+    if (col_amax && writer) {
+      col_amax[(int64_t)e * k + 2 * tid] = __uint_as_float(cpair << 16);
+      col_amax[(int64_t)e * k + 2 * tid + 1] = __uint_as_float(cpair & 0xFFFF0000u);
+    }
+  }
+  __syncthreads();  // every partial read before the final pairs replace them
+  if ((uint32_t)tid < kp) l_cp[tid] = cpair;
+  __syncthreads();
+
+  // rowwise: a 16-element block per thread and pass (block q of the slice
+  // is elements 16q .. 16q+15: row q / nb, block q % nb)
+  if (row_data) {
+    for (uint32_t q = tid + g * kSmallThreads; q < me * nb; q += kSmallSplit * kSmallThreads) {
+      const uint32_t i = q / nb, b = q % nb;
+      const u32x4 q0 = l_x[2 * q], q1 = l_x[2 * q + 1];
+      const uint32_t bm = l_bm[q];
+      const float s = __uint_as_float((uint32_t)l_ra[i] << 16) / 2688.0f;
+      float m;
+      const uint32_t S = block_step(__uint_as_float(bm << 16), s, 1.0f / s, &m);
+      uint32_t p0 = 0, p1 = 0;
+      p0 = FP4X2(p0, bf16lo(q0.x) * m, bf16hi(q0.x) * m, 0);
+      p0 = FP4X2(p0, bf16lo(q0.y) * m, bf16hi(q0.y) * m, 1);
+      p0 = FP4X2(p0, bf16lo(q0.z) * m, bf16hi(q0.z) * m, 2);
+      p0 = FP4X2(p0, bf16lo(q0.w) * m, bf16hi(q0.w) * m, 3);
+      p1 = FP4X2(p1, bf16lo(q1.x) * m, bf16hi(q1.x) * m, 0);
+      p1 = FP4X2(p1, bf16lo(q1.y) * m, bf16hi(q1.y) * m, 1);
+      p1 = FP4X2(p1, bf16lo(q1.z) * m, bf16hi(q1.z) * m, 2);
+      p1 = FP4X2(p1, bf16lo(q1.w) * m, bf16hi(q1.w) * m, 3);
+      *reinterpret_cast<u32x2*>(row_data + (int64_t)(rbeg + i) * (k / 2) + 8 * b) = u32x2{p0, p1};
+      row_scale[(int64_t)(rbeg + i) * (k / 16) + b] = (uint8_t)S;
+    }
+  }
+  // columnwise: a 16-row block of a column per thread and pass (adjacent
+  // threads take adjacent columns)
+  if (col_data) {
+    const uint32_t nrb = me / 16;
+    uint8_t* cd = col_data + (int64_t)k * rbeg / 2;
+    uint8_t* cs = col_scale + (int64_t)k * rbeg / 16;
+    for (uint32_t q = tid + g * kSmallThreads; q < ku * nrb; q += kSmallSplit * kSmallThreads) {
+      const uint32_t c = q % ku, rb = q / ku;
+      uint32_t w[16], bm = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        w[i] = lx16[(16 * rb + i) * ku + c];
+        bm = max(bm, w[i] & 0x7FFFu);
+      }
+      const uint32_t pm = l_cp[c >> 1];
+      const float s = __uint_as_float(((c & 1) ? (pm >> 16) : (pm & 0xFFFFu)) << 16) / 2688.0f;
+      float m;
+      const uint32_t S = block_step(__uint_as_float(bm << 16), s, 1.0f / s, &m);
+      uint32_t p0 = 0, p1 = 0;
+      p0 = FP4X2(p0, __uint_as_float(w[0] << 16) * m, __uint_as_float(w[1] << 16) * m, 0);
+      p0 = FP4X2(p0, __uint_as_float(w[2] << 16) * m, __uint_as_float(w[3] << 16) * m, 1);
+      p0 = FP4X2(p0, __uint_as_float(w[4] << 16) * m, __uint_as_float(w[5] << 16) * m, 2);
+      p0 = FP4X2(p0, __uint_as_float(w[6] << 16) * m, __uint_as_float(w[7] << 16) * m, 3);
+      p1 = FP4X2(p1, __uint_as_float(w[8] << 16) * m, __uint_as_float(w[9] << 16) * m, 0);
+      p1 = FP4X2(p1, __uint_as_float(w[10] << 16) * m, __uint_as_float(w[11] << 16) * m, 1);
+      p1 = FP4X2(p1, __uint_as_float(w[12] << 16) * m, __uint_as_float(w[13] << 16) * m, 2);
+      p1 = FP4X2(p1, __uint_as_float(w[14] << 16) * m, __uint_as_float(w[15] << 16) * m, 3);
+      *reinterpret_cast<u32x2*>(cd + (int64_t)c * (me / 2) + 8 * rb) = u32x2{p0, p1};
+      cs[(int64_t)c * (me / 16) + rb] = (uint8_t)S;
+    }
+  }
+}
+
 // ------------------------------------------------------------- host side
 
 int check_cast_outputs(const float* row_amax, const float* col_amax, const uint8_t* row_data,
@@ -522,6 +674,26 @@ int launch_rowwise_fused(const uint16_t* x, int64_t rows, int64_t k, const Routi
   else
     hipLaunchKernelGGL(group_quantize_rowwise_kernel<16>, dim3(grid), dim3(kThreads), 0, st, x, k, R, row_amax,
                        row_data, row_scale);
+  return hip_status();
+}
+
+// One launch for small inputs with a columnwise output (see the kernel):
+// every expert's rows times k within the limit -- for host splits the
+// largest expert, for device routing the capacity (any expert may hold it).
+bool small_input(int64_t max_expert_rows, int64_t k) {
+  return max_expert_rows * k <= kSmallMaxExpertElems && k <= kSmallMaxK;
+}
+int64_t max_expert_rows(const Routing& R) {
+  int64_t mx = 0;
+  for (int e = 0; e < R.num_experts; ++e)
+    mx = std::max<int64_t>(mx, (int64_t)R.h_offs[e] - (e ? R.h_offs[e - 1] : 0));
+  return mx;
+}
+
+int launch_small(const uint16_t* x, int64_t k, const Routing& R, float* row_amax, float* col_amax,
+                 uint8_t* row_data, uint8_t* row_scale, uint8_t* col_data, uint8_t* col_scale, hipStream_t st) {
+  hipLaunchKernelGGL(group_quantize_small_kernel, dim3((unsigned)R.num_experts * kSmallSplit), dim3(kSmallThreads), 0, st, x,
+                     k, R, row_data ? row_amax : nullptr, col_amax, row_data, row_scale, col_data, col_scale);
   return hip_status();
 }
 
@@ -589,6 +761,8 @@ int nvfp4_group_quantize(const uint16_t* x, int64_t sum_m, int64_t k, int32_t nu
   hipStream_t st = (hipStream_t)stream;
   if (row_data && !col_data && k <= kRowFusedMaxK)
     return launch_rowwise_fused(x, sum_m, k, R, row_amax, row_data, row_scale, st);
+  if (col_data && small_input(max_expert_rows(R), k))
+    return launch_small(x, k, R, row_amax, col_amax, row_data, row_scale, col_data, col_scale, st);
   if ((rc = launch_amax(x, sum_m, k, R, row_data ? row_amax : nullptr, col_data ? col_amax : nullptr, st)))
     return rc;
   return launch_cast(x, sum_m, k, R, row_amax, col_amax, row_data, row_scale, col_data, col_scale, st);
@@ -606,6 +780,8 @@ int nvfp4_group_quantize_graphsafe(const uint16_t* x, int64_t m_capacity, int64_
   hipStream_t st = (hipStream_t)stream;
   if (row_data && !col_data && k <= kRowFusedMaxK)
     return launch_rowwise_fused(x, m_capacity, k, R, row_amax, row_data, row_scale, st);
+  if (col_data && small_input(m_capacity, k))
+    return launch_small(x, k, R, row_amax, col_amax, row_data, row_scale, col_data, col_scale, st);
   if ((rc = launch_amax(x, m_capacity, k, R, row_data ? row_amax : nullptr, col_data ? col_amax : nullptr,
                         st)))
     return rc;

@@ -35,6 +35,7 @@ KERNEL_SOURCES = {
     "group_amax_kernel": "nvfp4_group.hip",
     "amax_init_kernel": "nvfp4_group.hip",
     "group_quantize_rowwise_kernel": "nvfp4_group.hip",
+    "group_quantize_small_kernel": "nvfp4_group.hip",
     "dequant_kernel": "nvfp4_dequant.hip",
     "gemm_fwd_kernel": "nvfp4_gemm.hip",
     "gemm_wgrad_kernel": "nvfp4_gemm.hip",

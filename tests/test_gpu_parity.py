@@ -155,7 +155,7 @@ def test_deterministic():
 
 # ----------------------------------------------------------- graph-safe path
 
-def _graphsafe(x_dev, E, offs, m_cap, rowwise=True, columnwise=True, prefill=None):
+def _graphsafe(x_dev, E, offs, m_cap, rowwise=True, columnwise=True, prefill=None, entry="two_calls"):
     k = x_dev.shape[1]
     out = alloc(m_cap, k, E, rowwise, columnwise)
     if prefill is not None:
@@ -164,8 +164,11 @@ def _graphsafe(x_dev, E, offs, m_cap, rowwise=True, columnwise=True, prefill=Non
     d_offs = torch.tensor(offs, dtype=torch.int32, device="cuda:0")
     d_status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     t = tensors(out)
-    B.nvfp4_group_amax_graphsafe(x_dev, E, d_offs, d_status, t["row_amax"], t["col_amax"])
-    B.nvfp4_group_cast_graphsafe(x_dev, E, d_offs, d_status, **t)
+    if entry == "two_calls":
+        B.nvfp4_group_amax_graphsafe(x_dev, E, d_offs, d_status, t["row_amax"], t["col_amax"])
+        B.nvfp4_group_cast_graphsafe(x_dev, E, d_offs, d_status, **t)
+    else:
+        B.nvfp4_group_quantize_graphsafe(x_dev, E, d_offs, d_status, **t)
     torch.cuda.synchronize()
     return out, int(d_status.item())
 
@@ -307,3 +310,59 @@ def test_max_host_experts_mostly_empty():
     splits = [0] * 512
     splits[0], splits[200], splits[511] = 128, 256, 128
     check_small(synth.random_case(65, splits, 32, "normal"))
+
+
+# Small inputs with a columnwise output: nvfp4_group_quantize runs them as one
+# launch (one work-group per expert); the bytes must be the oracle's.
+SMALL_ONE_LAUNCH = [
+    ([128, 0, 256, 128], 256, "normal", 91),        # the tiny workload's shape (largest expert at the limit)
+    ([4096], 16, "normal", 92),                     # k = 16: the most rows one expert may have
+    ([0, 128, 0], 512, "outliers", 93),             # k at its limit
+    ([128, 0, 128], 272, "rowscale", 94),           # ragged 512-column chunk
+    ([1280, 512], 48, "student", 95),               # gradient-like values, long experts
+    ([128, 128, 128], 16, "sparse", 96),            # all-zero blocks and rows
+]
+
+
+@pytest.mark.parametrize("splits,k,dist,seed", SMALL_ONE_LAUNCH)
+def test_small_input_one_launch(splits, k, dist, seed):
+    assert max(splits) * k <= B.SMALL_MAX_EXPERT_ELEMS and k <= B.SMALL_MAX_K
+    check_small(synth.random_case(seed, splits, k, dist), entry="quantize")
+
+
+def test_small_input_one_launch_columnwise_only():
+    check_small(synth.random_case(97, [256, 0, 128], 96, "rowscale"), rowwise=False, columnwise=True,
+                entry="quantize")
+
+
+def test_small_input_graphsafe_one_launch():
+    # buffers for 512 rows, routing covers 384: the one-launch graph-safe
+    # path writes the oracle's bytes and leaves rows 384.. as they were
+    rng = np.random.default_rng(98)
+    cap, k = 512, 96
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((cap, k)).astype(np.float32))
+    splits = [256, 0, 128]
+    assert cap * k <= B.SMALL_MAX_EXPERT_ELEMS
+    log("graph-safe one launch, partial routing")
+    gs, status = _graphsafe(to_device(xb), 3, B.offsets_from_splits(splits), cap, prefill=0x5A, entry="quantize")
+    assert status == 0
+    assert_guards(gs)
+    g = to_numpy(gs)
+    tot = sum(splits)
+    assert (g["row_amax"][tot:].view(np.uint32) == 0x5A5A5A5A).all()
+    assert (g["row_data"][tot:] == 0x5A).all() and (g["row_scale"][tot:] == 0x5A).all()
+    assert (g["col_data"][k * tot // 2:] == 0x5A).all() and (g["col_scale"][k * tot // 16:] == 0x5A).all()
+    ref = oracle_ref(synth.Workload("partial", xb[:tot], np.array(splits, np.int64)))
+    for key, n in (("row_amax", tot), ("row_data", tot), ("row_scale", tot), ("col_amax", None),
+                   ("col_data", k * tot // 2), ("col_scale", k * tot // 16)):
+        assert first_mismatch(g[key][:n] if n is not None else g[key], ref[key]) is None, key
+
+
+def test_small_input_graphsafe_rejects_bad_routing():
+    log("graph-safe one launch, bad device routing")
+    x = torch.zeros((1024, 32), dtype=torch.int16, device="cuda:0")
+    gs, status = _graphsafe(x, 3, [256, 128, 384], 1024, prefill=0x33, entry="quantize")
+    assert status & B.NVFP4G_DEV_NONMONO
+    assert_guards(gs)
+    for key, g in to_numpy(gs).items():
+        assert (g.view(np.uint8) == 0x33).all(), key

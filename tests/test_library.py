@@ -40,6 +40,24 @@ def test_header_declares_the_boundary():
     }
 
 
+def test_binding_constants_match_the_header():
+    """Every integer macro of the header that the binding mirrors has the
+    header's value (status codes, device status bits, size limits, the
+    one-launch small-input limits)."""
+    from nvfp4_block_scaled_group_amd import binding
+    text = open(os.path.join(ROOT, "include", "nvfp4_group.h")).read()
+    checked = set()
+    for name, expr in re.findall(r"#define (NVFP4G_\w+) (\(?-?[0-9]+(?: << [0-9]+)?\)?)", text):
+        e = expr.strip("()")
+        value = (int(e.split("<<")[0]) << int(e.split("<<")[1])) if "<<" in e else int(e)
+        for attr in (name, name[len("NVFP4G_"):]):
+            if hasattr(binding, attr):
+                assert getattr(binding, attr) == value, (name, getattr(binding, attr), value)
+                checked.add(attr)
+    assert {"NVFP4G_OK", "NVFP4G_EHIP", "NVFP4G_DEV_OVERFLOW", "MAX_EXPERTS_HOST", "MAX_EXPERTS_DEVICE",
+            "SMALL_MAX_EXPERT_ELEMS", "SMALL_MAX_K"} <= checked
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
