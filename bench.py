@@ -86,9 +86,15 @@ class TimingEvents:
         return ev
 
     def record(self, ev):
-        rc = self.hip.hipEventRecord(ev, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        rc = self.hip.hipEventRecord(ev, self._stream())
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def _stream(self):
+        raw = getattr(self.torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:  # the current stream's handle, without building a Stream object
+            return ctypes.c_void_p(raw(self.torch.cuda.current_device()))
+        return ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
 
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()

@@ -112,8 +112,15 @@ def _x(x: torch.Tensor):
     return _ptr(x), x.shape[0], x.shape[1]
 
 
+# the current stream's raw handle without building a Stream object (~0.1 us
+# against ~3 us per call for torch.cuda.current_stream())
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
+        if _raw_current_stream is not None:
+            return ctypes.c_void_p(_raw_current_stream(torch.cuda.current_device()))
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 

@@ -366,3 +366,12 @@ def test_small_input_graphsafe_rejects_bad_routing():
     assert_guards(gs)
     for key, g in to_numpy(gs).items():
         assert (g.view(np.uint8) == 0x33).all(), key
+
+
+def test_binding_launches_on_torch_current_stream():
+    # the binding passes the handle of torch's current stream (the null
+    # stream by default, a side stream inside torch.cuda.stream(...))
+    assert (B._stream(None).value or 0) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert (B._stream(None).value or 0) == side.cuda_stream != 0
