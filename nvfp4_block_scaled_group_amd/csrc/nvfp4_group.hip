@@ -464,13 +464,15 @@ __global__ __launch_bounds__(kThreads) void group_quantize_rowwise_kernel(
 // Small inputs in one launch.  When every expert holds at most
 // kSmallMaxExpertElems elements (K <= kSmallMaxK follows, an expert having
 // 128 rows or none), the general path's three launches (zero-fill, amax,
-// cast; ~6 us each, mostly launch latency) cost more than the work.  One
-// workgroup per expert runs the whole path: it copies the expert's rows (one
-// contiguous slice of x, at most 128 KB) into LDS with every load in flight
-// at once, takes the row and column amax there (each written once, so with
-// no zero-fill and no atomics), then the rowwise and columnwise block steps
-// from LDS -- the cast kernel's line scales, block step and FP4 converts, so
-// the bytes are the same.
+// cast; ~6 us each, mostly launch latency) cost more than the work.
+// kSmallSplit workgroups per expert each run the whole path: copy the
+// expert's rows (one contiguous slice of x, at most 128 KB) into LDS with
+// every load in flight at once, take the row and column amax there, then
+// encode their share of the rowwise and columnwise blocks from LDS -- the
+// cast kernel's line scales, block step and FP4 converts, so the bytes are
+// the same.  The first of them writes the amax outputs (each element once,
+// so with no zero-fill and no atomics); computing the amax in each one costs
+// less than leaving all the encoding to one workgroup on one CU.
 constexpr int64_t kSmallMaxExpertElems = NVFP4G_SMALL_MAX_EXPERT_ELEMS;
 constexpr int64_t kSmallMaxK = NVFP4G_SMALL_MAX_K;
 static_assert(kSmallMaxK * 128 == kSmallMaxExpertElems, "K limit = elements of a 128-row expert");
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(kSmallThreads) void group_quantize_small_kernel(
   }
   uint32_t cpair = 0;
   if ((uint32_t)tid < kp) {
-    for (uint32_t g = 0; g < nseg; ++g) cpair = pkmax(cpair, l_cp[g * kp + tid]);
+    for (uint32_t sg = 0; sg < nseg; ++sg) cpair = pkmax(cpair, l_cp[sg * kp + tid]);
     if (col_amax && writer) {
       col_amax[(int64_t)e * k + 2 * tid] = __uint_as_float(cpair << 16);
       col_amax[(int64_t)e * k + 2 * tid + 1] = __uint_as_float(cpair & 0xFFFF0000u);

@@ -10,8 +10,8 @@ with ``--calib-copy``, which adds a plain 1 GiB device copy.  FETCH_SIZE and
 WRITE_SIZE (KiB per dispatch) are scaled by what they read for that copy of
 known size (1 GiB read, 1 GiB written), giving HBM bytes per launch.  Each
 kernel's entry records the SHA-256 of the sources it is built from (its .hip
-file and the shared headers); the benchmark reports a kernel's traffic only
-while those sources are unchanged.  ``--kernels`` limits a summary to some
+file and the shared headers, comments aside); the benchmark reports a
+kernel's traffic only while that code is unchanged.  ``--kernels`` limits a summary to some
 kernels (plus the calibration copy).
 """
 from __future__ import annotations
@@ -22,10 +22,12 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
+ABI_HEADER = os.path.join(os.path.dirname(PKG), "include", "nvfp4_group.h")
 COPY_BYTES = 1 << 30
 # kernel -> the .hip file that defines it; the longer names come first, since
 # names are matched as substrings of the profiler's kernel names
@@ -43,13 +45,23 @@ KERNEL_SOURCES = {
 KERNELS = tuple(KERNEL_SOURCES)
 
 
+def _code(text: str) -> str:
+    """Source text without comments, blank lines and indentation: what the
+    compiler sees, so that editing a comment keeps a measurement valid."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.strip() for line in text.splitlines() if line.strip())
+
+
 def source_sha256(kernel: str) -> str:
-    """SHA-256 over the kernel's .hip file and every shared header."""
+    """SHA-256 over the code of the kernel's .hip file, the shared headers and
+    the C ABI header (its macros set sizes the kernels use)."""
     h = hashlib.sha256()
     files = [KERNEL_SOURCES[kernel]] + sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
-    for name in files:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    paths = [os.path.join(CSRC, f) for f in files] + [ABI_HEADER]
+    for path in paths:
+        with open(path) as f:
+            h.update(os.path.basename(path).encode() + b"\0" + _code(f.read()).encode())
     return h.hexdigest()
 
 
