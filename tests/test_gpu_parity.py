@@ -229,11 +229,14 @@ def test_graphsafe_rejects_bad_device_routing(offs, bits):
         assert (g.view(np.uint8) == 0x33).all(), key
 
 
-def test_graph_capture_replays_under_new_routing():
+@pytest.mark.parametrize("E,cap,k", [
+    (8, 2048, 400),   # the general path (zero-fill, amax, cast)
+    (4, 256, 256),    # capacity * k at the one-launch limit: the small-input kernel
+])
+def test_graph_capture_replays_under_new_routing(E, cap, k):
     # one capture, replays with new routing written to the device offsets;
     # every replay equals the host-split path on that routing, byte for byte
     rng = np.random.default_rng(47)
-    E, cap, k = 8, 2048, 400
     xb = synth.f32_to_bf16_bits((rng.standard_t(3.0, (cap, k)) * 1e-3).astype(np.float32))
     x = to_device(xb)
     out = alloc(cap, k, E, True, True)
