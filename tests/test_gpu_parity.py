@@ -378,3 +378,27 @@ def test_binding_launches_on_torch_current_stream():
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         assert (B._stream(None).value or 0) == side.cuda_stream != 0
+
+
+def _sweep_cases(n=16, seed=2024):
+    rng = np.random.default_rng(seed)
+    dists = ["normal", "outliers", "rowscale", "student", "sparse"]
+    cases = []
+    for i in range(n):
+        # even cases fit the one-launch limit (<= 256 rows per expert, k <= 256)
+        small = i % 2 == 0
+        E = int(rng.integers(1, 13))
+        units = rng.integers(0, 3 if small else 4, E)  # groups of 128 rows, empty experts included
+        if units.sum() == 0:
+            units[int(rng.integers(0, E))] = 1
+        k = 16 * int(rng.integers(1, 17 if small else 66))  # 16 .. 256 / 16 .. 1040
+        cases.append(([int(u) * 128 for u in units], k, dists[i % len(dists)], 300 + i))
+    return cases
+
+
+@pytest.mark.parametrize("splits,k,dist,seed", _sweep_cases())
+@pytest.mark.parametrize("entry", ["two_calls", "quantize"])
+def test_random_sweep(splits, k, dist, seed, entry):
+    # seeded random shapes and value mixes through both host entries (the
+    # quantize entry takes the one-launch path where the experts are small)
+    check_small(synth.random_case(seed, splits, k, dist), entry=entry)
