@@ -185,7 +185,7 @@ def cpu_baseline(w, target_rows: int = 16384, max_workers: int = 16) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--settle-ms", type=float, default=150.0,
                     help="untimed steps for this long before the warmup steps: the GPU's clocks ramp up over "
