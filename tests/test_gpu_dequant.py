@@ -139,3 +139,25 @@ def test_dequant_columnwise_many_small_experts_and_partial_routing():
     got = b.cpu().numpy()
     assert first_mismatch(got[:n], out.numpy()[:n]) is None
     assert (got[n:] == -7.0).all()
+
+
+@pytest.mark.parametrize("offs,bits", [
+    ([256, 128, 384], B.NVFP4G_DEV_NONMONO),
+    ([256, 300, 384], B.NVFP4G_DEV_UNALIGNED),
+    ([256, 384, 1280], B.NVFP4G_DEV_OVERFLOW),
+])
+def test_dequant_columnwise_graphsafe_rejects_bad_routing(offs, bits):
+    # bad device routing: the status bits are set and no output element is written
+    rng = np.random.default_rng(76)
+    cap, k = 1024, 64
+    col_data = torch.from_numpy(rng.integers(0, 256, cap * k // 2, dtype=np.uint8)).cuda()
+    col_scale = torch.from_numpy(rng.integers(0x20, 0x50, cap * k // 16, dtype=np.uint8)).cuda()
+    col_amax = torch.ones(3 * k, dtype=torch.float32, device="cuda:0")
+    out = torch.full((cap * k,), -7.0, dtype=torch.float32, device="cuda:0")
+    d_offs = torch.tensor(offs, dtype=torch.int32, device="cuda:0")
+    d_status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    log(f"dequant graph-safe bad routing {offs}")
+    B.nvfp4_group_dequant_columnwise_graphsafe(col_data, col_scale, col_amax, cap, k, 3, d_offs, out, d_status)
+    torch.cuda.synchronize()
+    assert int(d_status.item()) & bits
+    assert bool((out == -7.0).all())

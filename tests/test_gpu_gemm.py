@@ -259,3 +259,37 @@ def test_wgrad_graphsafe_equals_host_split_and_replays():
         assert int(d_status.item()) == 0
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {i}"
         log(f"wgrad replay {i}: routing {sp} byte-identical to the host-split call")
+
+
+@pytest.mark.parametrize("offs,bits", [
+    ([256, 128, 384], B.NVFP4G_DEV_NONMONO),
+    ([256, 300, 384], B.NVFP4G_DEV_UNALIGNED),
+    ([256, 384, 1280], B.NVFP4G_DEV_OVERFLOW),
+])
+def test_graphsafe_gemms_reject_bad_routing(offs, bits):
+    # bad device routing: both graph-safe GEMMs set the status bits and write
+    # no output element
+    rng = np.random.default_rng(94)
+    E, n, k, m_cap = 3, 48, 128, 1024
+    u8 = lambda *s: dev(rng.integers(0, 256, s, dtype=np.uint8))
+    sc = lambda *s: dev(rng.integers(0x20, 0x50, s, dtype=np.uint8))
+    amax = lambda m: dev(rng.uniform(0.5, 2.0, m).astype(np.float32))
+    d_offs = torch.tensor(offs, dtype=torch.int32, device="cuda:0")
+    log(f"graph-safe GEMMs, bad routing {offs}")
+
+    out = torch.full((m_cap, n), -7.0, dtype=torch.float32, device="cuda:0")
+    d_status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    B.nvfp4_group_gemm_graphsafe(u8(m_cap, k // 2), sc(m_cap, k // 16), amax(m_cap),
+                                 u8(E, n, k // 2), sc(E, n, k // 16), amax(E * n), d_offs, out, d_status)
+    torch.cuda.synchronize()
+    assert int(d_status.item()) & bits
+    assert bool((out == -7.0).all())
+
+    dw = torch.full((E, n, k), -7.0, dtype=torch.float32, device="cuda:0")
+    d_status.zero_()
+    B.nvfp4_group_gemm_wgrad_graphsafe(u8(m_cap * n // 2), sc(m_cap * n // 16), amax(E * n),
+                                       u8(m_cap * k // 2), sc(m_cap * k // 16), amax(E * k),
+                                       m_cap, E, d_offs, n, k, dw, d_status)
+    torch.cuda.synchronize()
+    assert int(d_status.item()) & bits
+    assert bool((dw == -7.0).all())
