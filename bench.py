@@ -50,7 +50,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "grouped NVFP4 amax+cast HBM GB/s (bytes in+out) and % of MI355X peak BW"
-TRAFFIC_FILE = "profiles/group_cast_kernel-deepseek_share_e32_k7168_m65536.md"
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, per workload
+TRAFFIC_FILES = {"deepseek_share": "profiles/group_cast_kernel-deepseek_share_e32_k7168_m65536.md",
+                 "down_proj": "profiles/group_cast_kernel-down_proj_e64_k2048_m131072.md"}
 
 
 class TimingEvents:
@@ -279,8 +281,9 @@ def main():
         kernels = {dom_name: {"avg_us": round(dom_ms * 1e3, 2), "GBps": round(dom_bytes / dom_ms / 1e6, 2)}}
     else:
         dom_name, dom_ms, dom_bytes = "group_cast_kernel", second_ms, nbytes["cast_kernel"]
-        kernels = {"amax (init + group_amax_kernel)": {"avg_us": round(first_ms * 1e3, 2),
-                                                       "GBps": round(nbytes["amax_kernel"] / first_ms / 1e6, 2)},
+        amax_name = "group_amax_rows_kernel" if k <= 2048 else "group_amax_kernel"
+        kernels = {f"amax (init + {amax_name})": {"avg_us": round(first_ms * 1e3, 2),
+                                                  "GBps": round(nbytes["amax_kernel"] / first_ms / 1e6, 2)},
                    "group_cast_kernel": {"avg_us": round(second_ms * 1e3, 2),
                                          "GBps": round(nbytes["cast_kernel"] / second_ms / 1e6, 2)}}
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -288,8 +291,8 @@ def main():
     # HBM bytes per launch of the cast kernel from the committed FETCH_SIZE /
     # WRITE_SIZE summary, only while the HIP source is the one it was taken on
     from nvfp4_block_scaled_group_amd import profiling
-    traffic = (profiling.load_traffic(os.path.join(ROOT, TRAFFIC_FILE), dom_name)
-               if args.workload == "deepseek_share" else None)
+    traffic_file = TRAFFIC_FILES.get(args.workload)
+    traffic = profiling.load_traffic(os.path.join(ROOT, traffic_file), dom_name) if traffic_file else None
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -307,7 +310,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic["bytes"] if traffic else None,
-                     "traffic_source": TRAFFIC_FILE if traffic else None,
+                     "traffic_source": traffic_file if traffic else None,
                      "avg_us": round(dom_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": dom_bytes},
         "kernels": kernels,

@@ -35,6 +35,7 @@ KERNEL_SOURCES = {
     "mxfp4_group_cast_kernel": "mxfp4_group.hip",
     "group_cast_kernel": "nvfp4_group.hip",
     "group_amax_kernel": "nvfp4_group.hip",
+    "group_amax_rows_kernel": "nvfp4_group.hip",
     "amax_init_kernel": "nvfp4_group.hip",
     "group_quantize_rowwise_kernel": "nvfp4_group.hip",
     "group_quantize_small_kernel": "nvfp4_group.hip",
