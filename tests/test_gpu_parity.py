@@ -275,6 +275,18 @@ def test_graph_capture_replays_under_new_routing(E, cap, k):
 
 # ------------------------------------------------------- more shapes / entries
 
+@pytest.mark.parametrize("k", [512, 528, 1040, 1552, 2032])
+def test_amax_row_tiles_ragged_k_and_uneven_ranges(k):
+    # K <= 2048 takes the amax that reads whole rows (1 - 4 column chunks per
+    # lane); 70 row groups give more tiles than work-groups, so ranges are
+    # uneven and experts change inside a work-group's range
+    rng = np.random.default_rng(k)
+    units = rng.integers(0, 5, 24)
+    units[-1] += 70 - int(units.sum()) if units.sum() < 70 else 0
+    w = synth.random_case(70 + k, [int(u) * 128 for u in units], k, "rowscale")
+    check_small(w)
+
+
 @pytest.mark.parametrize("k", [16, 528, 2048, 2064, 4096, 8192, 8208])
 def test_rowwise_quantize_fused_and_fallback(k):
     # K <= 8192 runs the one-pass rowwise kernel (4, 8 or 16 column segments
