@@ -36,7 +36,8 @@
 //    time (32 bytes per line, 16 per lane, double-buffered): copied per step
 //    (8 bytes per line, 4 per lane) the scales took a third of the copy
 //    instructions for a ninth of the bytes.  Each wave decodes its own
-//    fragments right before the MFMAs: v_cvt_scalef32_pk_f16_fp4 with unit
+//    fragments one sub-step ahead of the MFMAs, interleaved with them
+//    (one MFMA to six VALU instructions): v_cvt_scalef32_pk_f16_fp4 with unit
 //    scale gives the exact E2M1 values two at a time, one packed fp16
 //    multiply applies value(S) (converted once per block pair by
 //    v_cvt_scalef32_pk_f16_fp8).
@@ -270,18 +271,37 @@ __device__ __forceinline__ void gemm_tile(const OperandTile& A, const OperandTil
       wb[in][0] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 16 * swz(line, 2 * h));
       wb[in][1] = *reinterpret_cast<const u32x4*>(base + kStB + kRowBytes * line + 16 * swz(line, 2 * h + 1));
     }
+    // Sub-step s+1's fragments are decoded while sub-step s's MFMAs run, and
+    // the scheduler is told to alternate one MFMA with six VALU instructions
+    // (the decode is 48 per sub-step for 8 MFMAs), so each wave keeps its own
+    // matrix core busy during its decode instead of leaving that to the other
+    // wave on the SIMD.
+    h8_t af[2][kWM], bf[2][kWN];
+#pragma unroll
+    for (int im = 0; im < kWM; ++im) af[0][im] = decode8(wa[im][0][0], sa[im][0][0]);
+#pragma unroll
+    for (int in = 0; in < kWN; ++in) bf[0][in] = decode8(wb[in][0][0], sb[in][0][0]);
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      h8_t af[kWM], bf[kWN];
+      const int cu = s & 1, nx = cu ^ 1, t = s + 1;
+      if (t < kBK / 16) {
 #pragma unroll
-      for (int im = 0; im < kWM; ++im) af[im] = decode8(wa[im][s >> 2][s & 3], sa[im][s >> 2][(s >> 1) & 1]);
+        for (int im = 0; im < kWM; ++im) af[nx][im] = decode8(wa[im][t >> 2][t & 3], sa[im][t >> 2][(t >> 1) & 1]);
 #pragma unroll
-      for (int in = 0; in < kWN; ++in) bf[in] = decode8(wb[in][s >> 2][s & 3], sb[in][s >> 2][(s >> 1) & 1]);
+        for (int in = 0; in < kWN; ++in) bf[nx][in] = decode8(wb[in][t >> 2][t & 3], sb[in][t >> 2][(t >> 1) & 1]);
+      }
 #pragma unroll
       for (int im = 0; im < kWM; ++im)
 #pragma unroll
         for (int in = 0; in < kWN; ++in)
-          acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[im], bf[in], acc[im][in], 0, 0, 0);
+          acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cu][im], bf[cu][in], acc[im][in], 0, 0, 0);
+      if (t < kBK / 16) {
+#pragma unroll
+        for (int i = 0; i < kWM * kWN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+        }
+      }
     }
   };
   issue(0, lds0);
