@@ -124,35 +124,44 @@ def algorithmic_bytes(sum_m: int, k: int, E: int, rowwise: bool, columnwise: boo
     return {"amax_kernel": amax_k, "cast_kernel": cast_k, "step": amax_k + cast_k}
 
 
-_SAMPLE_X = None  # the sample's rows, inherited by the forked oracle workers
-_TASK_ROWS = 1024  # rows per rowwise task
-_TASK_COLS = 1024  # columns per columnwise task
+def host_cpu() -> dict:
+    """What the host offers the CPU baseline: CPU model, online CPUs, the CPUs
+    this process may run on, and the worker threads the oracle uses."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": affinity}
 
 
-def _oracle_task(task) -> None:
-    rowwise, lo, hi, c0, c1 = task
+def cpu_baseline(w, one_thread_rows: int = 16384, threads: int | None = None) -> dict:
+    """The oracle, as it stands, on the whole workload: independent oracle
+    calls (the rowwise direction on row ranges, the columnwise direction on
+    column ranges of each expert; together exactly the bytes of one call) on
+    a pool of host threads, at most one per CPU of the process's share and at
+    most 16 (a one-GPU share of the GPU host).  Also one call on one thread
+    over the first whole experts (in expert order) that fit in
+    ``one_thread_rows`` rows.  Runs before the process touches the GPU."""
     from oracle import oracle as O
-    x = _SAMPLE_X[lo:hi] if rowwise else np.ascontiguousarray(_SAMPLE_X[lo:hi, c0:c1])
-    O.group_quantize(x, [hi - lo], rowwise, not rowwise)
-
-
-def cpu_baseline(w, target_rows: int = 16384, max_workers: int = 16) -> dict:
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    whole experts (in expert order, skipping any that would overshoot) up to
-    ``target_rows`` rows, both directions.  Timed on one thread (one call),
-    then on the host's cores (at most ``max_workers`` forked processes) as
-    independent oracle calls: the rowwise direction on row ranges and the
-    columnwise direction on column ranges of each expert (rows are
-    independent in the rowwise output and columns in the columnwise one, so
-    together the calls produce the same bytes as the single call).  Runs
-    before the process touches the GPU, so that forking is safe."""
-    global _SAMPLE_X
-    import multiprocessing
-    from oracle import oracle as O
+    from oracle import parallel as OP
+    n = threads or OP.default_threads()
+    t0 = time.perf_counter()
+    OP.group_quantize(w.x, w.splits, w.rowwise, w.columnwise, threads=n)
+    dtn = time.perf_counter() - t0
+    b_all = algorithmic_bytes(w.sum_m, w.k, w.num_experts, w.rowwise, w.columnwise)["step"]
     offs = np.concatenate([[0], np.cumsum(w.splits)])
     chosen, rows = [], 0
     for e, m in enumerate(w.splits):
-        if m and rows + int(m) <= target_rows:
+        if m and rows + int(m) <= one_thread_rows:
             chosen.append(e)
             rows += int(m)
     xs = np.concatenate([w.x[offs[e]:offs[e + 1]] for e in chosen])
@@ -160,28 +169,120 @@ def cpu_baseline(w, target_rows: int = 16384, max_workers: int = 16) -> dict:
     t0 = time.perf_counter()
     O.group_quantize(xs, sp, w.rowwise, w.columnwise)
     dt1 = time.perf_counter() - t0
-    _SAMPLE_X = xs
-    so = np.concatenate([[0], np.cumsum(sp)]).astype(int)
-    tasks = []
-    for i in range(len(sp)):
-        lo, hi = int(so[i]), int(so[i + 1])
-        if w.rowwise:
-            tasks += [(True, r, min(r + _TASK_ROWS, hi), 0, w.k) for r in range(lo, hi, _TASK_ROWS)]
-        if w.columnwise:
-            tasks += [(False, lo, hi, c, min(c + _TASK_COLS, w.k)) for c in range(0, w.k, _TASK_COLS)]
-    tasks.sort(key=lambda t: (t[2] - t[1]) * (t[4] - t[3]), reverse=True)
-    workers = max(1, min(max_workers, os.cpu_count() or 1, len(tasks)))
-    with multiprocessing.get_context("fork").Pool(workers) as pool:
-        t0 = time.perf_counter()
-        list(pool.imap_unordered(_oracle_task, tasks))
-        dtn = time.perf_counter() - t0
-    _SAMPLE_X = None
-    b = algorithmic_bytes(rows, w.k, len(sp), w.rowwise, w.columnwise)["step"]
-    return {"value": round(b / dtn / 1e9, 5), "unit": "GB/s", "cores": workers, "kind": "oracle",
-            "sample": f"{len(sp)} whole experts, {rows} of {w.sum_m} rows x K={w.k} (both directions), "
-                      f"C oracle: {len(tasks)} row-range / column-range calls over {workers} processes "
-                      f"{dtn:.2f} s, one call on one thread {dt1:.2f} s",
-            "value_one_thread": round(b / dt1 / 1e9, 5)}
+    b1 = algorithmic_bytes(rows, w.k, len(sp), w.rowwise, w.columnwise)["step"]
+    ntasks = len(OP.tasks(w.splits, w.k, w.rowwise, w.columnwise))
+    res = {"value": round(b_all / dtn / 1e9, 5), "unit": "GB/s", "cores": n, "kind": "oracle",
+           "sample": f"the whole workload ({w.sum_m} rows x K={w.k}, both directions): {ntasks} row-range / "
+                     f"column-range calls of the C oracle on {n} threads, {dtn:.2f} s",
+           "seconds": round(dtn, 3), "threads": n,
+           "value_one_thread": round(b1 / dt1 / 1e9, 5),
+           "one_thread_sample": f"one call on one thread: {len(sp)} whole experts, {rows} rows, {dt1:.2f} s"}
+    res.update(host_cpu())
+    return res
+
+
+WORKLOADS = ["deepseek_share", "down_proj", "outliers", "tiny"]
+# the other configurations reported beside the headline, with their timed steps
+SIDE_CONFIGS = {"tiny": 1000, "outliers": 1000, "down_proj": 200}
+
+
+def measure_step(B, torch, tev, w, x, out, steps: int, warmup: int, settle_ms: float) -> dict:
+    """Time `steps` back-to-back steps of the whole path on workload `w` (x and
+    the outputs already on the device): wall clock between two device
+    synchronisations, plus per-launch times from HIP events on the stream."""
+    splits = [int(v) for v in w.splits]
+    k = w.k
+    fused = w.rowwise and not w.columnwise
+    # small inputs with a columnwise output: the library's one-launch path
+    small = w.columnwise and max(splits) * k <= B.SMALL_MAX_EXPERT_ELEMS and k <= B.SMALL_MAX_K
+
+    def step(ev=None):
+        if ev is not None:
+            tev.record(ev[0])
+        if fused or small:
+            # rowwise only: one pass (row amax and cast together); small
+            # inputs: one launch, eight work-groups per expert
+            B.nvfp4_group_quantize(x, splits, **out)
+            if ev is not None:
+                tev.record(ev[1])
+                tev.record(ev[2])
+            return
+        B.nvfp4_group_amax(x, splits, out["row_amax"], out["col_amax"])
+        if ev is not None:
+            tev.record(ev[1])
+        B.nvfp4_group_cast(x, splits, **out)
+        if ev is not None:
+            tev.record(ev[2])
+
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        step()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[tev.new() for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    first_ms = float(np.mean([tev.elapsed_ms(e[0], e[1]) for e in events]))
+    second_ms = float(np.mean([tev.elapsed_ms(e[1], e[2]) for e in events]))
+    nbytes = algorithmic_bytes(w.sum_m, k, w.num_experts, w.rowwise, w.columnwise)
+    ms_per_step = wall * 1e3 / steps
+    if fused or small:
+        dom_name = "group_quantize_rowwise_kernel" if fused else "group_quantize_small_kernel"
+        dom_ms, dom_bytes = first_ms, nbytes["fused_kernel"] if fused else nbytes["step"]
+        kernels = {dom_name: {"avg_us": round(dom_ms * 1e3, 2), "GBps": round(dom_bytes / dom_ms / 1e6, 2)}}
+        entry = ("nvfp4_group_quantize (host splits, fused rowwise pass)" if fused
+                 else "nvfp4_group_quantize (host splits, one launch for a small input)")
+    else:
+        dom_name, dom_ms, dom_bytes = "group_cast_kernel", second_ms, nbytes["cast_kernel"]
+        amax_name = "group_amax_rows_kernel" if k <= 2048 else "group_amax_kernel"
+        kernels = {f"amax (init + {amax_name})": {"avg_us": round(first_ms * 1e3, 2),
+                                                  "GBps": round(nbytes["amax_kernel"] / first_ms / 1e6, 2)},
+                   "group_cast_kernel": {"avg_us": round(second_ms * 1e3, 2),
+                                         "GBps": round(nbytes["cast_kernel"] / second_ms / 1e6, 2)}}
+        entry = "nvfp4_group_amax + nvfp4_group_cast (host splits)"
+    return {"steps": steps, "ms_per_step": ms_per_step, "first_ms": first_ms, "second_ms": second_ms,
+            "nbytes": nbytes, "dom_name": dom_name, "dom_ms": dom_ms, "dom_bytes": dom_bytes,
+            "kernels": kernels, "entry": entry, "step": step}
+
+
+def directions(w) -> str:
+    return "+".join(d for d, on in (("rowwise", w.rowwise), ("columnwise", w.columnwise)) if on)
+
+
+def roofline(profiling, workload: str, kernel: str, nbytes: int, ms: float) -> dict:
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic_file = TRAFFIC_FILES.get(workload)
+    traffic = profiling.load_traffic(os.path.join(ROOT, traffic_file), kernel) if traffic_file else None
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic["bytes"] if traffic else None,
+            "traffic_source": traffic_file if traffic else None, "avg_us": round(ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": nbytes}
+
+
+def side_config(B, synth, torch, tev, profiling, dev, name: str, steps: int) -> dict:
+    """One of the other configurations: the same step protocol (shorter), its
+    rate against the HBM peak, the kernels' event times, and (where a profile
+    exists) the dominant kernel's measured traffic."""
+    print(f"[bench] config {name}", file=sys.stderr, flush=True)
+    w = synth.CONFIGS[name]()
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    out = B.alloc_outputs(w.sum_m, w.k, w.num_experts, w.rowwise, w.columnwise, device=dev)
+    r = measure_step(B, torch, tev, w, x, out, steps, max(20, steps // 10), 30.0)
+    gbs = r["nbytes"]["step"] / (r["ms_per_step"] * 1e-3) / 1e9
+    res = {"workload": w.name, "directions": directions(w), "entry": r["entry"], "steps": steps,
+           "ms_per_step": round(r["ms_per_step"], 5), "GBps": round(gbs, 2),
+           "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": r["nbytes"]["step"],
+           "gpu_ms_per_step": round(r["first_ms"] + r["second_ms"], 5), "kernels": r["kernels"],
+           "roofline": roofline(profiling, name, r["dom_name"], r["dom_bytes"], r["dom_ms"])}
+    del x, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -192,15 +293,16 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=150.0,
                     help="untimed steps for this long before the warmup steps: the GPU's clocks ramp up over "
                          "the first tens of milliseconds of load on a fresh box (0: skip)")
-    ap.add_argument("--workload", default="deepseek_share",
-                    choices=["deepseek_share", "down_proj", "outliers", "tiny"])
+    ap.add_argument("--workload", default="deepseek_share", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other configurations")
     ap.add_argument("--graph-replays", type=int, default=100)
     ap.add_argument("--next-rows", type=int, default=20,
                     help="launches timed for each of the MXFP4 cast and the two dequants (0: skip)")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="also time the steps with a read of this many MB before each (outside the timed "
                          "events), so that no input or output is left in the 256 MB memory-side cache (0: skip)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the memory-ceiling kernels")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (3 times, untimed) so that a "
                          "rocprofv3 --pmc run can scale FETCH_SIZE / WRITE_SIZE by a copy of known size")
@@ -221,6 +323,7 @@ def main():
 
     import torch
     from nvfp4_block_scaled_group_amd import binding as B
+    from nvfp4_block_scaled_group_amd import profiling
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -228,92 +331,24 @@ def main():
     E, k, m = w.num_experts, w.k, w.sum_m
     x = torch.from_numpy(w.x.view(np.int16)).to(dev)
     out = B.alloc_outputs(m, k, E, w.rowwise, w.columnwise, device=dev)
-    nbytes = algorithmic_bytes(m, k, E, w.rowwise, w.columnwise)
-
-    fused = w.rowwise and not w.columnwise
-    # small inputs with a columnwise output: the library's one-launch path
-    small = w.columnwise and max(splits) * k <= B.SMALL_MAX_EXPERT_ELEMS and k <= B.SMALL_MAX_K
-
     tev = TimingEvents(torch)
 
-    def step(ev=None):
-        if ev is not None:
-            tev.record(ev[0])
-        if fused or small:
-            # rowwise only: one pass (row amax and cast together); small
-            # inputs: one launch, one work-group per expert
-            B.nvfp4_group_quantize(x, splits, **out)
-            if ev is not None:
-                tev.record(ev[1])
-                tev.record(ev[2])
-            return
-        B.nvfp4_group_amax(x, splits, out["row_amax"], out["col_amax"])
-        if ev is not None:
-            tev.record(ev[1])
-        B.nvfp4_group_cast(x, splits, **out)
-        if ev is not None:
-            tev.record(ev[2])
-
-    print(f"[bench] settle {args.settle_ms:.0f} ms, warmup {args.warmup}", file=sys.stderr, flush=True)
-    t_settle = time.perf_counter()
-    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
-        step()
-        torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[tev.new() for _ in range(3)] for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    first_ms = float(np.mean([tev.elapsed_ms(e[0], e[1]) for e in events]))
-    second_ms = float(np.mean([tev.elapsed_ms(e[1], e[2]) for e in events]))
-    ms_per_step = wall * 1e3 / args.steps
+    print(f"[bench] settle {args.settle_ms:.0f} ms, warmup {args.warmup}, timing {args.steps} steps",
+          file=sys.stderr, flush=True)
+    r = measure_step(B, torch, tev, w, x, out, args.steps, args.warmup, args.settle_ms)
+    ms_per_step, nbytes, step = r["ms_per_step"], r["nbytes"], r["step"]
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    if fused or small:
-        dom_name, dom_ms = ("group_quantize_rowwise_kernel", first_ms) if fused else \
-            ("group_quantize_small_kernel", first_ms)
-        dom_bytes = nbytes["fused_kernel"] if fused else nbytes["step"]
-        kernels = {dom_name: {"avg_us": round(dom_ms * 1e3, 2), "GBps": round(dom_bytes / dom_ms / 1e6, 2)}}
-    else:
-        dom_name, dom_ms, dom_bytes = "group_cast_kernel", second_ms, nbytes["cast_kernel"]
-        amax_name = "group_amax_rows_kernel" if k <= 2048 else "group_amax_kernel"
-        kernels = {f"amax (init + {amax_name})": {"avg_us": round(first_ms * 1e3, 2),
-                                                  "GBps": round(nbytes["amax_kernel"] / first_ms / 1e6, 2)},
-                   "group_cast_kernel": {"avg_us": round(second_ms * 1e3, 2),
-                                         "GBps": round(nbytes["cast_kernel"] / second_ms / 1e6, 2)}}
-    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
-
-    # HBM bytes per launch of the cast kernel from the committed FETCH_SIZE /
-    # WRITE_SIZE summary, only while the HIP source is the one it was taken on
-    from nvfp4_block_scaled_group_amd import profiling
-    traffic_file = TRAFFIC_FILES.get(args.workload)
-    traffic = profiling.load_traffic(os.path.join(ROOT, traffic_file), dom_name) if traffic_file else None
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "num_experts": E, "k": k, "sum_m": m,
-                   "directions": "+".join(d for d, on in (("rowwise", w.rowwise), ("columnwise", w.columnwise))
-                                          if on),
-                   "entry": ("nvfp4_group_quantize (host splits, fused rowwise pass)" if fused
-                             else "nvfp4_group_quantize (host splits, one launch for a small input)" if small
-                             else "nvfp4_group_amax + nvfp4_group_cast (host splits)"),
-                   "algorithmic_bytes_per_step": nbytes["step"],
+        "config": {"workload": w.name, "num_experts": E, "k": k, "sum_m": m, "directions": directions(w),
+                   "entry": r["entry"], "algorithmic_bytes_per_step": nbytes["step"],
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic["bytes"] if traffic else None,
-                     "traffic_source": traffic_file if traffic else None,
-                     "avg_us": round(dom_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": dom_bytes},
-        "kernels": kernels,
+        "roofline": roofline(profiling, args.workload, r["dom_name"], r["dom_bytes"], r["dom_ms"]),
+        "kernels": r["kernels"],
     }
 
     if args.flush_mb > 0:
@@ -334,10 +369,11 @@ def main():
         result["flushed_step"] = {"flush_mb": args.flush_mb, "steps": args.steps,
                                   "ms_per_step": round(f_ms, 4),
                                   "GBps": round(nbytes["step"] / (f_ms * 1e-3) / 1e9, 2),
-                                  "unflushed_event_ms_per_step": round(first_ms + second_ms, 4)}
+                                  "unflushed_event_ms_per_step": round(r["first_ms"] + r["second_ms"], 4)}
         del flush
 
-    result["hbm_ceiling"] = copy_ceiling(torch, tev, dev)
+    if not args.no_ceiling:
+        result["hbm_ceiling"] = hbm_ceiling(torch, tev, dev, w, x, out)
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -349,9 +385,17 @@ def main():
 
     if w.rowwise and w.columnwise and args.next_rows > 0:
         result["next_rows"] = next_rows(B, torch, tev, x, splits, out, E, k, m, args.next_rows)
+    del x, out
+    torch.cuda.empty_cache()
 
-    if args.workload == "deepseek_share" and args.graph_replays > 0:
-        result["graph_replay"] = graph_replay(B, synth, torch, tev, dev, args.graph_replays)
+    if not args.no_configs:
+        configs = {}
+        for name, n in SIDE_CONFIGS.items():
+            if name != args.workload:
+                configs[name] = side_config(B, synth, torch, tev, profiling, dev, name, n)
+        if args.graph_replays > 0:
+            configs["graph_replay"] = graph_replay(B, synth, torch, tev, dev, args.graph_replays)
+        result["configs"] = configs
 
     if cpu is not None:
         result["cpu_baseline"] = cpu
@@ -359,26 +403,90 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def copy_ceiling(torch, tev, dev, nbytes: int = 1 << 30, reps: int = 10) -> dict:
-    """Context for roofline.frac: a plain device-to-device copy of 1 GiB on
-    the same GPU in the same process (bytes read + written over its time,
-    HIP events on the same stream), the rate a stream that mixes reads and
-    writes reaches on this memory system."""
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+class Probe:
+    """The memory-ceiling kernels of probe/libhbmprobe.so, on torch's current stream."""
+
+    def __init__(self, tev):
+        path = os.path.join(ROOT, "nvfp4_block_scaled_group_amd", "probe", "libhbmprobe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m nvfp4_block_scaled_group_amd.build`")
+        self.L = ctypes.CDLL(path)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        self.L.hbm_probe_read.argtypes = [P, I64, P, I, P]
+        self.L.hbm_probe_fill.argtypes = [P, I64, I, P]
+        self.L.hbm_probe_copy.argtypes = [P, P, I64, I, P]
+        self.L.hbm_probe_mix.argtypes = [P, P, I64, I, P]
+        self.L.hbm_probe_cast_pattern.argtypes = [P, I64, I64, ctypes.c_int32, P, P, P, P, P, P]
+        self.tev = tev
+
+    def call(self, fn, *args):
+        rc = getattr(self.L, fn)(*args, self.tev._stream())
+        if rc != 0:
+            raise RuntimeError(f"{fn} failed ({rc})")
+
+
+def hbm_ceiling(torch, tev, dev, w, x, out, reps: int = 10) -> dict:
+    """Context for roofline.frac, measured in the same process with kernels
+    written here (probe/hbm_probe.hip): a 1 GiB read, fill and copy (the best
+    grid of a sweep), the cast's read/write ratio in its simplest layout
+    (64 KB read and 36 KB written contiguously per work-group), and the
+    cast's own loads and stores with no arithmetic, on this workload's
+    buffers; torch's device copy beside them."""
+    print("[bench] memory ceiling", file=sys.stderr, flush=True)
+    pr = Probe(tev)
+    G = 1 << 30
+    src = torch.empty(G, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    evs = [(tev.new(), tev.new()) for _ in range(reps)]
-    for e0, e1 in evs:
-        tev.record(e0)
-        dst.copy_(src)
-        tev.record(e1)
-    torch.cuda.synchronize()
-    ms = float(np.mean([tev.elapsed_ms(a, b) for a, b in evs]))
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(tev.new(), tev.new()) for _ in range(reps)]
+        for e0, e1 in evs:
+            tev.record(e0)
+            fn()
+            tev.record(e1)
+        torch.cuda.synchronize()
+        return float(np.mean([tev.elapsed_ms(a, b) for a, b in evs]))
+
+    def rate(name, ms, nbytes, **extra):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        d = {"kind": name, "avg_us": round(ms * 1e3, 2), "bytes": nbytes, "GBps": round(gbs, 2),
+             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        d.update(extra)
+        return d
+
+    def best(fn_of_grid, grids=(512, 1024, 2048, 4096, 8192)):
+        times = {g: timed(lambda g=g: fn_of_grid(g)) for g in grids}
+        g = min(times, key=times.get)
+        return times[g], g
+
+    res = {}
+    ms, g = best(lambda g: pr.call("hbm_probe_read", p(src), G, p(sink), g))
+    res["read"] = rate("1 GiB read, non-temporal 16-byte loads", ms, G, grid=g)
+    ms, g = best(lambda g: pr.call("hbm_probe_fill", p(dst), G, g))
+    res["fill"] = rate("1 GiB written, streaming 16-byte stores", ms, G, grid=g)
+    ms, g = best(lambda g: pr.call("hbm_probe_copy", p(src), p(dst), G, g))
+    res["copy"] = rate("1 GiB read + 1 GiB written, non-temporal loads and streaming stores", ms, 2 * G, grid=g)
+    ms = timed(lambda: pr.call("hbm_probe_mix", p(src), p(dst), G, 9))
+    res["cast_ratio_mix"] = rate("1 GiB read + 576 MiB written (64 KB read and 36 KB written contiguously per "
+                                 "work-group, the cast's ratio)", ms, G + G // 16 * 9)
+    ms = timed(lambda: dst.copy_(src))
+    res["torch_copy"] = rate("torch device copy_, 1 GiB read + 1 GiB written", ms, 2 * G)
     del src, dst
-    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
-    return {"kind": "device copy, 1 GiB read + 1 GiB written", "avg_us": round(ms * 1e3, 2),
-            "GBps": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    torch.cuda.empty_cache()
+    if w.rowwise and w.columnwise and w.k % 256 == 0 and w.num_experts <= 512:
+        sp = (ctypes.c_int64 * w.num_experts)(*[int(v) for v in w.splits])
+        N = w.sum_m * w.k
+        ms = timed(lambda: pr.call("hbm_probe_cast_pattern", p(x), w.sum_m, w.k, w.num_experts, sp,
+                                   p(out["row_data"]), p(out["row_scale"]), p(out["col_data"]),
+                                   p(out["col_scale"])))
+        res["cast_pattern_no_arithmetic"] = rate(
+            "the cast kernel's loads and stores on this workload's buffers, no arithmetic", ms,
+            2 * N + 2 * (N // 2 + N // 16))
+    return res
 
 
 def next_rows(B, torch, tev, x, splits, out, E: int, k: int, m: int, reps: int) -> dict:
@@ -504,16 +612,20 @@ def library_gemm_rows(torch, timed, splits, n: int, k: int, m: int, dev) -> dict
 
 def graph_replay(B, synth, torch, tev, dev, replays: int) -> dict:
     """Graph-safe path on the expert-share shapes with gradient-like values:
-    one hipGraph capture of amax + cast, replayed with new routing written to
-    the device offsets before each replay (the offset copy is outside the
-    timed launches)."""
+    one hipGraph capture of amax + cast, replayed with new seeded routing
+    written to the device offsets before each replay (outside the timed
+    launch).  Every replay is checked: its outputs and a second output set
+    are filled with different sentinel bytes first; after the replay the
+    host-split path writes the second set for the same routing and the two
+    are compared on the device, so a byte left unwritten by either differs."""
     print("[bench] graph replay workload", file=sys.stderr, flush=True)
     w = synth.graph_replay()
     E, k, m = w.num_experts, w.k, w.sum_m
     x = torch.from_numpy(w.x.view(np.int16)).to(dev)
     out = B.alloc_outputs(m, k, E, True, True, device=dev)
-    routes = [torch.tensor(B.offsets_from_splits(synth.replay_splits(i)), dtype=torch.int32).pin_memory()
-              for i in range(replays)]
+    host = B.alloc_outputs(m, k, E, True, True, device=dev)
+    route_splits = [[int(v) for v in synth.replay_splits(i)] for i in range(replays)]
+    routes = [torch.tensor(B.offsets_from_splits(sp), dtype=torch.int32).pin_memory() for sp in route_splits]
     d_offs = torch.empty(E, dtype=torch.int32, device=dev)
     d_status = torch.zeros(1, dtype=torch.int32, device=dev)
     d_offs.copy_(routes[0])
@@ -526,19 +638,31 @@ def graph_replay(B, synth, torch, tev, dev, replays: int) -> dict:
     with torch.cuda.graph(g):
         B.nvfp4_group_quantize_graphsafe(x, E, d_offs, d_status, **out)
     torch.cuda.synchronize()
-    times = []
+    keys = [key for key, t in out.items() if t is not None]
+    times, identical = [], 0
     for i in range(replays):
         d_offs.copy_(routes[i], non_blocking=True)
+        for key in keys:
+            out[key].view(torch.uint8).fill_(0xA5)
+            host[key].view(torch.uint8).fill_(0x5A)
         e0, e1 = tev.new(), tev.new()
         tev.record(e0)
         g.replay()
         tev.record(e1)
         times.append((e0, e1))
+        B.nvfp4_group_amax(x, route_splits[i], host["row_amax"], host["col_amax"])
+        B.nvfp4_group_cast(x, route_splits[i], **host)
+        identical += int(all(torch.equal(out[key], host[key]) for key in keys))
     torch.cuda.synchronize()
     ms = float(np.mean([tev.elapsed_ms(a, b) for a, b in times]))
     nbytes = algorithmic_bytes(m, k, E, True, True)["step"]
-    return {"workload": w.name, "replays": replays, "ms_per_replay": round(ms, 4),
-            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 2), "status": int(d_status.item())}
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": w.name, "replays": replays, "ms_per_replay": round(ms, 4), "GBps": round(gbs, 2),
+           "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_replay": nbytes,
+           "byte_identical_to_host_split": identical, "status": int(d_status.item())}
+    del x, out, host
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

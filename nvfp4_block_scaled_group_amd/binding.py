@@ -106,10 +106,53 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+U8 = (torch.uint8,)
+F32 = (torch.float32,)
+I32 = (torch.int32,)
+X16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _current_device() -> torch.device:
+    return torch.device("cuda", torch.cuda.current_device())
+
+
+def _buf(name: str, t: Optional[torch.Tensor], dtypes, numel: int, required: bool = False):
+    """Pointer to a caller buffer after checking it on the host: on the
+    current device, contiguous, of one of ``dtypes`` and holding at least
+    ``numel`` elements (the kernels index it up to that size).  A wrong
+    buffer raises ValueError before anything is launched."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    dev = _current_device()
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected the current device {dev}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def _x(x: torch.Tensor):
-    if x.dim() != 2 or x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.dtype not in X16:
         raise ValueError("x must be a 2-D bf16 (or raw 16-bit) tensor")
-    return _ptr(x), x.shape[0], x.shape[1]
+    return _buf("x", x, X16, x.numel(), True), x.shape[0], x.shape[1]
+
+
+def _outputs(m: int, k: int, e: int, row_amax, col_amax, row_data, row_scale, col_data, col_scale):
+    return (_buf("row_amax", row_amax, F32, m), _buf("col_amax", col_amax, F32, e * k),
+            _buf("row_data", row_data, U8, m * k // 2), _buf("row_scale", row_scale, U8, m * k // 16),
+            _buf("col_data", col_data, U8, m * k // 2), _buf("col_scale", col_scale, U8, m * k // 16))
+
+
+def _routing(e: int, d_offs, d_status):
+    return _buf("d_offs", d_offs, I32, max(e, 1), True), _buf("d_status", d_status, I32, 1, True)
 
 
 # the current stream's raw handle without building a Stream object (~0.1 us
@@ -135,112 +178,156 @@ def _splits(h_splits: Sequence[int]):
 def nvfp4_group_amax(x, h_splits, row_amax=None, col_amax=None, stream=None):
     xp, m, k = _x(x)
     sp, e = _splits(h_splits)
-    _check("nvfp4_group_amax", load_library().nvfp4_group_amax(
-        xp, m, k, e, sp, _ptr(row_amax), _ptr(col_amax), _stream(stream)))
+    ra, ca = _buf("row_amax", row_amax, F32, m), _buf("col_amax", col_amax, F32, e * k)
+    _check("nvfp4_group_amax", load_library().nvfp4_group_amax(xp, m, k, e, sp, ra, ca, _stream(stream)))
 
 
 def nvfp4_group_cast(x, h_splits, row_amax=None, col_amax=None, row_data=None, row_scale=None,
                      col_data=None, col_scale=None, stream=None):
     xp, m, k = _x(x)
     sp, e = _splits(h_splits)
-    _check("nvfp4_group_cast", load_library().nvfp4_group_cast(
-        xp, m, k, e, sp, _ptr(row_amax), _ptr(col_amax), _ptr(row_data), _ptr(row_scale),
-        _ptr(col_data), _ptr(col_scale), _stream(stream)))
+    bufs = _outputs(m, k, e, row_amax, col_amax, row_data, row_scale, col_data, col_scale)
+    _check("nvfp4_group_cast", load_library().nvfp4_group_cast(xp, m, k, e, sp, *bufs, _stream(stream)))
 
 
 def nvfp4_group_quantize(x, h_splits, row_amax=None, col_amax=None, row_data=None, row_scale=None,
                          col_data=None, col_scale=None, stream=None):
     xp, m, k = _x(x)
     sp, e = _splits(h_splits)
-    _check("nvfp4_group_quantize", load_library().nvfp4_group_quantize(
-        xp, m, k, e, sp, _ptr(row_amax), _ptr(col_amax), _ptr(row_data), _ptr(row_scale),
-        _ptr(col_data), _ptr(col_scale), _stream(stream)))
+    bufs = _outputs(m, k, e, row_amax, col_amax, row_data, row_scale, col_data, col_scale)
+    _check("nvfp4_group_quantize", load_library().nvfp4_group_quantize(xp, m, k, e, sp, *bufs, _stream(stream)))
 
 
 def nvfp4_group_amax_graphsafe(x, num_experts, d_offs, d_status, row_amax=None, col_amax=None,
                                stream=None):
     xp, m, k = _x(x)
+    e = int(num_experts)
+    do, ds = _routing(e, d_offs, d_status)
+    ra, ca = _buf("row_amax", row_amax, F32, m), _buf("col_amax", col_amax, F32, e * k)
     _check("nvfp4_group_amax_graphsafe", load_library().nvfp4_group_amax_graphsafe(
-        xp, m, k, int(num_experts), _ptr(d_offs), _ptr(row_amax), _ptr(col_amax), _ptr(d_status),
-        _stream(stream)))
+        xp, m, k, e, do, ra, ca, ds, _stream(stream)))
 
 
 def nvfp4_group_cast_graphsafe(x, num_experts, d_offs, d_status, row_amax=None, col_amax=None,
                                row_data=None, row_scale=None, col_data=None, col_scale=None,
                                stream=None):
     xp, m, k = _x(x)
+    e = int(num_experts)
+    do, ds = _routing(e, d_offs, d_status)
+    bufs = _outputs(m, k, e, row_amax, col_amax, row_data, row_scale, col_data, col_scale)
     _check("nvfp4_group_cast_graphsafe", load_library().nvfp4_group_cast_graphsafe(
-        xp, m, k, int(num_experts), _ptr(d_offs), _ptr(row_amax), _ptr(col_amax), _ptr(row_data),
-        _ptr(row_scale), _ptr(col_data), _ptr(col_scale), _ptr(d_status), _stream(stream)))
+        xp, m, k, e, do, *bufs, ds, _stream(stream)))
 
 
 def nvfp4_group_quantize_graphsafe(x, num_experts, d_offs, d_status, row_amax=None, col_amax=None,
                                    row_data=None, row_scale=None, col_data=None, col_scale=None,
                                    stream=None):
     xp, m, k = _x(x)
+    e = int(num_experts)
+    do, ds = _routing(e, d_offs, d_status)
+    bufs = _outputs(m, k, e, row_amax, col_amax, row_data, row_scale, col_data, col_scale)
     _check("nvfp4_group_quantize_graphsafe", load_library().nvfp4_group_quantize_graphsafe(
-        xp, m, k, int(num_experts), _ptr(d_offs), _ptr(row_amax), _ptr(col_amax), _ptr(row_data),
-        _ptr(row_scale), _ptr(col_data), _ptr(col_scale), _ptr(d_status), _stream(stream)))
+        xp, m, k, e, do, *bufs, ds, _stream(stream)))
 
 
 def nvfp4_group_dequant_rowwise(row_data, row_scale, row_amax, out, stream=None):
     """row_data [rows, k/2] u8, row_scale [rows, k/16] u8, row_amax [rows] f32 -> out [rows, k] f32."""
+    if not isinstance(row_data, torch.Tensor) or row_data.dim() != 2:
+        raise ValueError("row_data must be a 2-D [rows, k/2] tensor")
     rows, half_k = row_data.shape
+    k = 2 * half_k
     _check("nvfp4_group_dequant_rowwise", load_library().nvfp4_group_dequant_rowwise(
-        _ptr(row_data), _ptr(row_scale), _ptr(row_amax), rows, 2 * half_k, _ptr(out), _stream(stream)))
+        _buf("row_data", row_data, U8, rows * half_k, True), _buf("row_scale", row_scale, U8, rows * k // 16, True),
+        _buf("row_amax", row_amax, F32, rows, True), rows, k, _buf("out", out, F32, rows * k, True),
+        _stream(stream)))
 
 
 def nvfp4_group_dequant_columnwise(col_data, col_scale, col_amax, h_splits, k, out, stream=None):
     """Transposed output (per expert [k, M_e] lines) -> out f32 in the same layout (k * sum_m values)."""
     sp, e = _splits(h_splits)
     sum_m = sum(int(v) for v in h_splits)
+    k = int(k)
     _check("nvfp4_group_dequant_columnwise", load_library().nvfp4_group_dequant_columnwise(
-        _ptr(col_data), _ptr(col_scale), _ptr(col_amax), sum_m, int(k), e, sp, _ptr(out), _stream(stream)))
+        _buf("col_data", col_data, U8, sum_m * k // 2, True), _buf("col_scale", col_scale, U8, sum_m * k // 16, True),
+        _buf("col_amax", col_amax, F32, e * k, True), sum_m, k, e, sp, _buf("out", out, F32, sum_m * k, True),
+        _stream(stream)))
 
 
 def nvfp4_group_dequant_columnwise_graphsafe(col_data, col_scale, col_amax, m_capacity, k, num_experts, d_offs,
                                              out, d_status, stream=None):
+    m, k, e = int(m_capacity), int(k), int(num_experts)
+    do, ds = _routing(e, d_offs, d_status)
     _check("nvfp4_group_dequant_columnwise_graphsafe",
            load_library().nvfp4_group_dequant_columnwise_graphsafe(
-               _ptr(col_data), _ptr(col_scale), _ptr(col_amax), int(m_capacity), int(k), int(num_experts),
-               _ptr(d_offs), _ptr(out), _ptr(d_status), _stream(stream)))
+               _buf("col_data", col_data, U8, m * k // 2, True), _buf("col_scale", col_scale, U8, m * k // 16, True),
+               _buf("col_amax", col_amax, F32, e * k, True), m, k, e, do, _buf("out", out, F32, m * k, True), ds,
+               _stream(stream)))
+
+
+def _mx_outputs(m: int, k: int, row_data, row_scale, col_data, col_scale):
+    return (_buf("row_data", row_data, U8, m * k // 2), _buf("row_scale", row_scale, U8, m * k // 32),
+            _buf("col_data", col_data, U8, m * k // 2), _buf("col_scale", col_scale, U8, m * k // 32))
 
 
 def mxfp4_group_cast(x, h_splits, row_data=None, row_scale=None, col_data=None, col_scale=None, stream=None):
     xp, m, k = _x(x)
     sp, e = _splits(h_splits)
-    _check("mxfp4_group_cast", load_library().mxfp4_group_cast(
-        xp, m, k, e, sp, _ptr(row_data), _ptr(row_scale), _ptr(col_data), _ptr(col_scale), _stream(stream)))
+    bufs = _mx_outputs(m, k, row_data, row_scale, col_data, col_scale)
+    _check("mxfp4_group_cast", load_library().mxfp4_group_cast(xp, m, k, e, sp, *bufs, _stream(stream)))
 
 
 def mxfp4_group_cast_graphsafe(x, num_experts, d_offs, d_status, row_data=None, row_scale=None, col_data=None,
                                col_scale=None, stream=None):
     xp, m, k = _x(x)
+    e = int(num_experts)
+    do, ds = _routing(e, d_offs, d_status)
+    bufs = _mx_outputs(m, k, row_data, row_scale, col_data, col_scale)
     _check("mxfp4_group_cast_graphsafe", load_library().mxfp4_group_cast_graphsafe(
-        xp, m, k, int(num_experts), _ptr(d_offs), _ptr(row_data), _ptr(row_scale), _ptr(col_data),
-        _ptr(col_scale), _ptr(d_status), _stream(stream)))
+        xp, m, k, e, do, *bufs, ds, _stream(stream)))
+
+
+def _gemm_fwd_operands(a_data, a_scale, a_amax, b_data, b_scale, b_amax, out):
+    if not isinstance(a_data, torch.Tensor) or a_data.dim() != 2:
+        raise ValueError("a_data must be a 2-D [rows, k/2] tensor")
+    if not isinstance(b_data, torch.Tensor) or b_data.dim() != 3:
+        raise ValueError("b_data must be a 3-D [E, n, k/2] tensor")
+    rows, half_k = a_data.shape
+    E, n = b_data.shape[0], b_data.shape[1]
+    if b_data.shape[2] != half_k:
+        raise ValueError(f"b_data has {2 * b_data.shape[2]} columns per line, a_data {2 * half_k}")
+    k = 2 * half_k
+    ptrs = (_buf("a_data", a_data, U8, rows * half_k, True), _buf("a_scale", a_scale, U8, rows * k // 16, True),
+            _buf("a_amax", a_amax, F32, rows, True), _buf("b_data", b_data, U8, E * n * half_k, True),
+            _buf("b_scale", b_scale, U8, E * n * k // 16, True), _buf("b_amax", b_amax, F32, E * n, True))
+    return ptrs, rows, E, n, k, _buf("out", out, F32, rows * n, True)
 
 
 def nvfp4_group_gemm(a_data, a_scale, a_amax, b_data, b_scale, b_amax, h_splits, out, stream=None):
     """Forward form: a_data [sum_m, k/2], a_scale [sum_m, k/16], a_amax [sum_m];
     b_data [E, n, k/2], b_scale [E, n, k/16], b_amax [E*n] -> out f32 [sum_m, n]."""
-    sum_m, half_k = a_data.shape
-    E, n = b_data.shape[0], b_data.shape[1]
+    ptrs, sum_m, E, n, k, op = _gemm_fwd_operands(a_data, a_scale, a_amax, b_data, b_scale, b_amax, out)
     sp, e = _splits(h_splits)
     if e != E:
         raise ValueError(f"{e} splits for {E} expert operands")
-    _check("nvfp4_group_gemm", load_library().nvfp4_group_gemm(
-        _ptr(a_data), _ptr(a_scale), _ptr(a_amax), _ptr(b_data), _ptr(b_scale), _ptr(b_amax), sum_m, n,
-        2 * half_k, e, sp, _ptr(out), _stream(stream)))
+    _check("nvfp4_group_gemm", load_library().nvfp4_group_gemm(*ptrs, sum_m, n, k, e, sp, op, _stream(stream)))
 
 
 def nvfp4_group_gemm_graphsafe(a_data, a_scale, a_amax, b_data, b_scale, b_amax, d_offs, out, d_status,
                                stream=None):
-    m_capacity, half_k = a_data.shape
-    E, n = b_data.shape[0], b_data.shape[1]
+    ptrs, m_capacity, E, n, k, op = _gemm_fwd_operands(a_data, a_scale, a_amax, b_data, b_scale, b_amax, out)
+    do, ds = _routing(E, d_offs, d_status)
     _check("nvfp4_group_gemm_graphsafe", load_library().nvfp4_group_gemm_graphsafe(
-        _ptr(a_data), _ptr(a_scale), _ptr(a_amax), _ptr(b_data), _ptr(b_scale), _ptr(b_amax), m_capacity, n,
-        2 * half_k, E, _ptr(d_offs), _ptr(out), _ptr(d_status), _stream(stream)))
+        *ptrs, m_capacity, n, k, E, do, op, ds, _stream(stream)))
+
+
+def _gemm_wgrad_operands(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax,
+                         m: int, e: int, n: int, k: int, out):
+    return (_buf("a_col_data", a_col_data, U8, m * n // 2, True),
+            _buf("a_col_scale", a_col_scale, U8, m * n // 16, True),
+            _buf("a_col_amax", a_col_amax, F32, e * n, True),
+            _buf("b_col_data", b_col_data, U8, m * k // 2, True),
+            _buf("b_col_scale", b_col_scale, U8, m * k // 16, True),
+            _buf("b_col_amax", b_col_amax, F32, e * k, True)), _buf("out", out, F32, e * n * k, True)
 
 
 def nvfp4_group_gemm_wgrad(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax, h_splits,
@@ -249,17 +336,21 @@ def nvfp4_group_gemm_wgrad(a_col_data, a_col_scale, a_col_amax, b_col_data, b_co
     per expert, X's with k) -> out f32 [E, n, k]."""
     sp, e = _splits(h_splits)
     sum_m = sum(int(v) for v in h_splits)
+    n, k = int(n), int(k)
+    ptrs, op = _gemm_wgrad_operands(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax,
+                                    sum_m, e, n, k, out)
     _check("nvfp4_group_gemm_wgrad", load_library().nvfp4_group_gemm_wgrad(
-        _ptr(a_col_data), _ptr(a_col_scale), _ptr(a_col_amax), _ptr(b_col_data), _ptr(b_col_scale),
-        _ptr(b_col_amax), sum_m, int(n), int(k), e, sp, _ptr(out), _stream(stream)))
+        *ptrs, sum_m, n, k, e, sp, op, _stream(stream)))
 
 
 def nvfp4_group_gemm_wgrad_graphsafe(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax,
                                      m_capacity, num_experts, d_offs, n, k, out, d_status, stream=None):
+    m, e, n, k = int(m_capacity), int(num_experts), int(n), int(k)
+    do, ds = _routing(e, d_offs, d_status)
+    ptrs, op = _gemm_wgrad_operands(a_col_data, a_col_scale, a_col_amax, b_col_data, b_col_scale, b_col_amax,
+                                    m, e, n, k, out)
     _check("nvfp4_group_gemm_wgrad_graphsafe", load_library().nvfp4_group_gemm_wgrad_graphsafe(
-        _ptr(a_col_data), _ptr(a_col_scale), _ptr(a_col_amax), _ptr(b_col_data), _ptr(b_col_scale),
-        _ptr(b_col_amax), int(m_capacity), int(n), int(k), int(num_experts), _ptr(d_offs), _ptr(out),
-        _ptr(d_status), _stream(stream)))
+        *ptrs, m, n, k, e, do, op, ds, _stream(stream)))
 
 
 # ---------------------------------------------------------------- helpers

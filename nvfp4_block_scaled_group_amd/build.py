@@ -3,7 +3,9 @@
     python -m nvfp4_block_scaled_group_amd.build
 
 Compiles ``csrc/*.hip`` with hipcc for gfx950 and links a plain shared library
-exporting the C ABI of ``include/nvfp4_group.h``.  The library's dependency on
+exporting the C ABI of ``include/nvfp4_group.h``; also builds
+``probe/libhbmprobe.so`` (the benchmark's memory-ceiling kernels, not part
+of that ABI).  The library's dependency on
 the HIP runtime is recorded as ``libamdhip64.so`` (the name PyTorch's ROCm
 build loads its own runtime under), so inside a process that already imported
 torch the library binds to that same runtime instead of loading a second one;
@@ -23,6 +25,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 BUILD_DIR = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libnvfp4g.so")
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libhbmprobe.so")
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
@@ -64,7 +68,21 @@ def build(verbose: bool = False) -> str:
         print(" ".join(link), flush=True)
     subprocess.check_call(link)
     os.replace(tmp, LIB)
+    build_probe(hipcc, verbose)
     return LIB
+
+
+def build_probe(hipcc: str, verbose: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, "hbm_probe.hip.o")
+    cmd = [hipcc, *HIPCC_FLAGS, "-c", PROBE_SRC, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.check_call(["g++", "-shared", "-o", tmp, obj, f"-L{_hip_runtime_dir()}", "-lamdhip64",
+                           f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}", "-Wl,--no-undefined"])
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

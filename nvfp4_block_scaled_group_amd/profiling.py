@@ -10,7 +10,7 @@ with ``--calib-copy``, which adds a plain 1 GiB device copy.  FETCH_SIZE and
 WRITE_SIZE (KiB per dispatch) are scaled by what they read for that copy of
 known size (1 GiB read, 1 GiB written), giving HBM bytes per launch.  Each
 kernel's entry records the SHA-256 of the sources it is built from (its .hip
-file and the shared headers, comments aside); the benchmark reports a
+file and the shared headers, comments aside, and the build flags); the benchmark reports a
 kernel's traffic only while that code is unchanged.  ``--kernels`` limits a summary to some
 kernels (plus the calibration copy).
 """
@@ -55,9 +55,12 @@ def _code(text: str) -> str:
 
 
 def source_sha256(kernel: str) -> str:
-    """SHA-256 over the code of the kernel's .hip file, the shared headers and
-    the C ABI header (its macros set sizes the kernels use)."""
+    """SHA-256 over the code of the kernel's .hip file, the shared headers,
+    the C ABI header (its macros set sizes the kernels use) and the compiler
+    flags the library is built with (a -D or -O change changes the code)."""
+    from . import build
     h = hashlib.sha256()
+    h.update(("flags\0" + " ".join(build.HIPCC_FLAGS) + "\0").encode())
     files = [KERNEL_SOURCES[kernel]] + sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
     paths = [os.path.join(CSRC, f) for f in files] + [ABI_HEADER]
     for path in paths:

@@ -58,6 +58,13 @@ def test_code_hash_ignores_comments_only():
     assert profiling._code(a) != profiling._code(c)
 
 
+def test_code_hash_covers_the_build_flags(monkeypatch):
+    from nvfp4_block_scaled_group_amd import build
+    before = profiling.source_sha256("group_cast_kernel")
+    monkeypatch.setattr(build, "HIPCC_FLAGS", build.HIPCC_FLAGS + ["-DNVFP4G_STORE_AUX=2"])
+    assert profiling.source_sha256("group_cast_kernel") != before
+
+
 def _summary(tmp_path, sha):
     data = {"workload": "w", "fetch_scale": 2.0, "write_scale": 1.0,
             "kernels": {"group_cast_kernel": {"fetch_bytes": 10, "write_bytes": 5, "source_sha256": sha}}}

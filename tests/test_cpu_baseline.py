@@ -1,6 +1,6 @@
-"""The benchmark's CPU baseline splits one oracle call into independent
-calls: the rowwise direction on row ranges and the columnwise direction on
-column ranges of each expert.  Rows are independent in the rowwise output
+"""The benchmark's CPU baseline (and the full-size parity tests) split one
+oracle call into independent calls: the rowwise direction on row ranges and
+the columnwise direction on column ranges of each expert.  Rows are independent in the rowwise output
 (each row has its own amax and blocks) and columns in the columnwise output
 (each column of an expert is its own line), so the pieces must reproduce the
 single call's bytes; this is checked here, and the baseline is run once on
@@ -36,6 +36,7 @@ def test_split_calls_reproduce_the_single_call():
 
 
 def test_cpu_baseline_runs_on_the_tiny_workload():
-    r = bench.cpu_baseline(synth.tiny(), max_workers=2)
+    r = bench.cpu_baseline(synth.tiny(), threads=2)
     assert r["kind"] == "oracle" and r["unit"] == "GB/s"
-    assert r["value"] > 0 and r["value_one_thread"] > 0 and 1 <= r["cores"] <= 2
+    assert r["value"] > 0 and r["value_one_thread"] > 0 and r["cores"] == r["threads"] == 2
+    assert r["nproc"] >= 1 and "whole workload" in r["sample"]

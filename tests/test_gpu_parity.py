@@ -1,9 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
-Small inputs are compared element by element (every amax, FP4 byte and E4M3
-scale, bit-exact); the full-size workloads are compared on sampled lines the
-oracle computes one by one, plus properties checked on every element (amax
-against torch's exact max, row/column amax consistency, guard bands).
+Inputs are compared element by element (every amax, FP4 byte and E4M3
+scale, bit-exact), with guard bands around every output; the full-size
+workloads are in test_gpu_fullsize.py.
 """
 import numpy as np
 import pytest
@@ -12,6 +11,7 @@ import torch
 from nvfp4_block_scaled_group_amd import binding as B
 from nvfp4_block_scaled_group_amd import synth
 from oracle import oracle as O
+from oracle import parallel as OP
 
 from gpu_helpers import (alloc, assert_equal_outputs, assert_guards, first_mismatch, log, run_host_split,
                          tensors, to_device, to_numpy)
@@ -275,16 +275,36 @@ def test_graph_capture_replays_under_new_routing(E, cap, k):
 
 # ------------------------------------------------------- more shapes / entries
 
+# rows per tile of the whole-row amax (K <= 2048): 4 waves x 16 / 8 / 4 / 4
+# rows for 1 / 2 / 3 / 4 column chunks of 512; its grid is min(rows/16, 512)
+AMAX_ROW_TILE = {1: 64, 2: 32, 3: 16, 4: 16}
+
+
 @pytest.mark.parametrize("k", [512, 528, 1040, 1552, 2032])
-def test_amax_row_tiles_ragged_k_and_uneven_ranges(k):
+def test_amax_row_tiles_ragged_k_and_long_ranges(k):
     # K <= 2048 takes the amax that reads whole rows (1 - 4 column chunks per
-    # lane); 70 row groups give more tiles than work-groups, so ranges are
-    # uneven and experts change inside a work-group's range
+    # lane).  Enough rows that every work-group walks at least 3 tiles (so the
+    # next-tile prefetch and the column flush on an expert change inside a
+    # range both run), with small experts so that ranges cross expert ends.
+    nch = (k + 511) // 512
+    tr = AMAX_ROW_TILE[nch]
+    grid = 512
+    rows = 3 * grid * tr + 128 * 5
     rng = np.random.default_rng(k)
-    units = rng.integers(0, 5, 24)
-    units[-1] += 70 - int(units.sum()) if units.sum() < 70 else 0
-    w = synth.random_case(70 + k, [int(u) * 128 for u in units], k, "rowscale")
-    check_small(w)
+    units, left = [], rows // 128
+    while left:
+        u = int(min(left, rng.integers(0, 4)))
+        units.append(u)
+        left -= u
+    splits = [u * 128 for u in units]
+    tiles = rows // tr
+    assert min(rows // 16, 512) == grid and tiles >= 3 * grid, (tiles, grid)
+    assert sum(1 for u in units if u == 0) >= 1 and len(units) > tiles // (3 * 16)
+    w = synth.random_case(70 + k, splits, k, "rowscale")
+    log(f"k={k} rows={rows} experts={len(splits)} tiles={tiles} grid={grid}")
+    out = run_host_split(to_device(w.x), splits)
+    assert_guards(out)
+    assert_equal_outputs(to_numpy(out), OP.group_quantize(w.x, splits))
 
 
 @pytest.mark.parametrize("k", [16, 528, 2048, 2064, 4096, 8192, 8208])
@@ -310,6 +330,32 @@ def test_rowwise_graphsafe_quantize_equals_host_split():
     assert_guards(out)
     assert_equal_outputs(to_numpy(out), host)
     assert_equal_outputs(host, oracle_ref(w, True, False), ["row_amax", "row_data", "row_scale"])
+
+
+@pytest.mark.parametrize("k", [1040, 4096, 8192, 8208])
+def test_rowwise_graphsafe_quantize_partial_routing(k):
+    # nvfp4_group_quantize_graphsafe with no columnwise output runs the fused
+    # rowwise pass (K <= 8192; K = 8208 falls back to amax + cast); buffers
+    # hold 1024 rows, the routing covers 640: rows 640.. keep their bytes and
+    # the routed rows equal the oracle
+    cap = 1024
+    splits = [256, 0, 384]
+    tot = sum(splits)
+    rng = np.random.default_rng(62 + k)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((cap, k)).astype(np.float32))
+    log(f"graph-safe rowwise quantize, partial routing, k={k}")
+    x = to_device(xb)
+    gs, status = _graphsafe(x, 3, B.offsets_from_splits(splits), cap, rowwise=True, columnwise=False,
+                            prefill=0x5A, entry="quantize")
+    assert status == 0
+    assert_guards(gs)
+    g = to_numpy(gs)
+    assert (g["row_amax"][tot:].view(np.uint32) == 0x5A5A5A5A).all()
+    assert (g["row_data"][tot:] == 0x5A).all() and (g["row_scale"][tot:] == 0x5A).all()
+    ref = O.group_quantize(xb[:tot], splits, True, False)
+    assert first_mismatch(g["row_amax"][:tot], ref["row_amax"]) is None
+    assert first_mismatch(g["row_data"][:tot], ref["row_data"]) is None
+    assert first_mismatch(g["row_scale"][:tot], ref["row_scale"]) is None
 
 
 def test_many_experts_and_one_expert():
