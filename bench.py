@@ -18,21 +18,26 @@ bytes count what the method must move: two reads of x (the column amax needs
 every row of an expert before any of its blocks can be cast), the amax
 vectors written once and read once, and both outputs written once.
 
-``flushed_step`` times the same steps with a 512 MB read before each
-(outside the events), so that the 256 MB memory-side cache holds nothing of
-the step's data; ``hbm_ceiling`` times a plain 1 GiB device copy in the same
-process, the practical rate of a stream of reads and writes; ``cpu_baseline``
-is the CPU oracle on a bounded sample, timed before the process touches the
-GPU.
-
-On workloads with both directions the JSON line also carries ``next_rows``:
-the grouped MXFP4 cast of the same input (one read of x, both MXFP4 outputs
-written), the rowwise / columnwise NVFP4 dequant of the step's outputs
-(codes, scales and line amax read once, fp32 written), and the row-scaled
-grouped GEMM (forward and weight gradient, MFMA-bound, TFLOP/s against the
-fp16 MFMA peak), each timed with HIP events over repeated launches; beside
-the GEMM, torch.matmul (hipBLASLt) in fp16 on operands of the same shapes,
-for context.
+Beside the headline the line carries:
+- ``configs``: the other workloads -- tiny (4 experts, one launch), outliers
+  (rowwise only, one fused pass), down_proj (64 experts, K=2048) -- each
+  timed with the same protocol, and graph_replay: one hipGraph capture of the
+  graph-safe step on the expert-share shapes replayed with 100 seeded
+  routings (timed back to back, then every routing checked byte for byte
+  against the host-split path on the device);
+- ``flushed_step``: the same steps with a 512 MB read before each (outside
+  the events), so that the 256 MB memory-side cache holds nothing of the
+  step's data and no dirty lines of the previous step;
+- ``hbm_ceiling``: what this memory system moves with kernels written here
+  (read, fill, copy with the best grid of a sweep, the cast's read/write
+  ratio in a contiguous layout, and the cast's own memory pattern with the
+  arithmetic removed) and torch's device copy;
+- ``next_rows``: the grouped MXFP4 cast of the same input, the rowwise /
+  columnwise NVFP4 dequant of the step's outputs, and the row-scaled grouped
+  GEMM (forward and weight gradient, MFMA-bound, TFLOP/s against the fp16
+  MFMA peak) with torch.matmul (hipBLASLt) fp16 on the same shapes beside it;
+- ``cpu_baseline``: the CPU oracle over the whole workload on the host's
+  threads (at most 16), timed before the process touches the GPU.
 """
 from __future__ import annotations
 
@@ -366,9 +371,12 @@ def main():
             step(fev[i])
         torch.cuda.synchronize()
         f_ms = float(np.mean([tev.elapsed_ms(e[0], e[2]) for e in fev]))
+        f1 = float(np.mean([tev.elapsed_ms(e[0], e[1]) for e in fev]))
         result["flushed_step"] = {"flush_mb": args.flush_mb, "steps": args.steps,
                                   "ms_per_step": round(f_ms, 4),
                                   "GBps": round(nbytes["step"] / (f_ms * 1e-3) / 1e9, 2),
+                                  "first_launch_us": round(f1 * 1e3, 2),
+                                  "second_launch_us": round((f_ms - f1) * 1e3, 2),
                                   "unflushed_event_ms_per_step": round(r["first_ms"] + r["second_ms"], 4)}
         del flush
 
@@ -614,10 +622,11 @@ def graph_replay(B, synth, torch, tev, dev, replays: int) -> dict:
     """Graph-safe path on the expert-share shapes with gradient-like values:
     one hipGraph capture of amax + cast, replayed with new seeded routing
     written to the device offsets before each replay (outside the timed
-    launch).  Every replay is checked: its outputs and a second output set
-    are filled with different sentinel bytes first; after the replay the
-    host-split path writes the second set for the same routing and the two
-    are compared on the device, so a byte left unwritten by either differs."""
+    launch), back to back.  Then every routing is replayed again and
+    checked: the graph's outputs and a second output set are filled with
+    different sentinel bytes first; after the replay the host-split path
+    writes the second set for the same routing and the two are compared on
+    the device, so a byte left unwritten by either differs."""
     print("[bench] graph replay workload", file=sys.stderr, flush=True)
     w = synth.graph_replay()
     E, k, m = w.num_experts, w.k, w.sum_m
@@ -639,17 +648,25 @@ def graph_replay(B, synth, torch, tev, dev, replays: int) -> dict:
         B.nvfp4_group_quantize_graphsafe(x, E, d_offs, d_status, **out)
     torch.cuda.synchronize()
     keys = [key for key, t in out.items() if t is not None]
-    times, identical = [], 0
+    # timing: replays back to back, new routing copied in before each
+    times = []
     for i in range(replays):
         d_offs.copy_(routes[i], non_blocking=True)
-        for key in keys:
-            out[key].view(torch.uint8).fill_(0xA5)
-            host[key].view(torch.uint8).fill_(0x5A)
         e0, e1 = tev.new(), tev.new()
         tev.record(e0)
         g.replay()
         tev.record(e1)
         times.append((e0, e1))
+    torch.cuda.synchronize()
+    # verification: the same routings again, each replay's outputs compared
+    # with the host-split path after sentinel fills
+    identical = 0
+    for i in range(replays):
+        d_offs.copy_(routes[i], non_blocking=True)
+        for key in keys:
+            out[key].view(torch.uint8).fill_(0xA5)
+            host[key].view(torch.uint8).fill_(0x5A)
+        g.replay()
         B.nvfp4_group_amax(x, route_splits[i], host["row_amax"], host["col_amax"])
         B.nvfp4_group_cast(x, route_splits[i], **host)
         identical += int(all(torch.equal(out[key], host[key]) for key in keys))
