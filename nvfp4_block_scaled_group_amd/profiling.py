@@ -6,7 +6,14 @@
 ``--stats`` is the output directory of ``rocprofv3 --kernel-trace --stats
 --output-format csv``; ``--fetch`` and ``--write`` those of two
 ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the same command
-with ``--calib-copy``, which adds a plain 1 GiB device copy.  FETCH_SIZE and
+with ``--calib-copy``, which adds a plain 1 GiB device copy; each optional
+``--counters DIR`` is a further ``--pmc`` run whose counters are tabulated per
+kernel (medians over dispatches), with the ratios they give where the
+counters are present.  GRBM_GUI_ACTIVE reads the sum over the 8 XCDs, so the
+kernel's busy cycles are GRBM_GUI_ACTIVE / 8: memory-unit busy =
+TA_BUSY_avr / (GRBM_GUI_ACTIVE / 8) (TA_BUSY_avr is the per-CU average),
+waves waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES, VALU busy =
+SQ_ACTIVE_INST_VALU * 4 / (1024 SIMDs * GRBM_GUI_ACTIVE / 8).  FETCH_SIZE and
 WRITE_SIZE (KiB per dispatch) are scaled by what they read for that copy of
 known size (1 GiB read, 1 GiB written), giving HBM bytes per launch.  Each
 kernel's entry records the SHA-256 of the sources it is built from (its .hip
@@ -104,8 +111,36 @@ def counter(dirname: str, name: str) -> dict:
     return {k: (max(v) if k == "copy" else statistics.median(v)) for k, v in vals.items()}
 
 
+SIMDS = 256 * 4  # MI355X: 256 compute units x 4 SIMDs
+XCDS = 8
+
+
+def all_counters(dirname: str) -> dict:
+    """kernel -> counter -> median over that kernel's dispatches."""
+    vals = {}
+    with open(_one(dirname, "*counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            vals.setdefault(_short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    return {k: {c: statistics.median(v) for c, v in cs.items()} for k, cs in vals.items()}
+
+
+def counter_ratios(c: dict) -> dict:
+    out = {}
+    gui = c.get("GRBM_GUI_ACTIVE", 0) / XCDS
+    if "TA_BUSY_avr" in c and gui:
+        out["mem_unit_busy"] = c["TA_BUSY_avr"] / gui
+    if "SQ_WAIT_ANY" in c and c.get("SQ_WAVE_CYCLES"):
+        out["waves_waiting"] = c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]
+    if "SQ_WAIT_INST_ANY" in c and c.get("SQ_WAVE_CYCLES"):
+        out["waves_waiting_on_issue"] = c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]
+    if "SQ_ACTIVE_INST_VALU" in c and gui:
+        out["valu_busy"] = c["SQ_ACTIVE_INST_VALU"] * 4 / (SIMDS * gui)
+    return out
+
+
 def summarize(stats_dir: str, fetch_dir: str, write_dir: str, cmd: str, workload: str,
-              kernels=None) -> tuple[str, dict]:
+              kernels=None, counter_dirs=()) -> tuple[str, dict]:
     keep = (lambda k: True) if not kernels else (lambda k: k in kernels or k == "copy")
     st = {k: v for k, v in kernel_stats(stats_dir).items() if keep(k)}
     fe = {k: v for k, v in counter(fetch_dir, "FETCH_SIZE").items() if keep(k)}
@@ -134,6 +169,26 @@ def summarize(stats_dir: str, fetch_dir: str, write_dir: str, cmd: str, workload
     for k, v in data["kernels"].items():
         lines.append(f"| {k} | {v['fetch_kib_raw']:.0f} | {v['write_kib_raw']:.0f} | {v['fetch_bytes']} | "
                      f"{v['write_bytes']} |")
+    extra = {}
+    for d in counter_dirs:
+        for k, cs in all_counters(d).items():
+            if keep(k) and k in KERNEL_SOURCES:
+                extra.setdefault(k, {}).update(cs)
+    if extra:
+        names = sorted({c for cs in extra.values() for c in cs})
+        lines += ["", "## Other counters (medians over dispatches) and the ratios they give", "",
+                  "```"] + [f"rocprofv3 --pmc {' '.join(sorted(all_counters(d)[next(iter(all_counters(d)))]))} "
+                            f"--output-format csv -d <dir> -o run -- {cmd}" for d in counter_dirs] + ["```", "",
+                  "| kernel | " + " | ".join(names) + " | mem unit busy | waves waiting | VALU busy |",
+                  "|---" * (len(names) + 4) + "|"]
+        for k, cs in extra.items():
+            r = counter_ratios(cs)
+            fmt = lambda v: f"{v:.3f}" if v is not None else "-"
+            lines.append(f"| {k} | " + " | ".join(f"{cs[n]:.4g}" if n in cs else "-" for n in names) +
+                         f" | {fmt(r.get('mem_unit_busy'))} | {fmt(r.get('waves_waiting'))} | "
+                         f"{fmt(r.get('valu_busy'))} |")
+            data["kernels"].setdefault(k, {})["counters"] = cs
+            data["kernels"][k]["ratios"] = {n: round(v, 4) for n, v in r.items()}
     lines += ["", "Machine-readable (read by bench.py; a kernel's entry is valid only while its sources "
               "have the SHA-256 it records):", "",
               "```json", json.dumps(data), "```", ""]
@@ -168,9 +223,10 @@ def main():
     ap.add_argument("--workload", default="deepseek_share_e32_k7168_m65536")
     ap.add_argument("--out", required=True)
     ap.add_argument("--kernels", default="", help="comma-separated kernel names to keep (default: all)")
+    ap.add_argument("--counters", action="append", default=[], help="output dir of a further --pmc run")
     a = ap.parse_args()
     kernels = [k for k in a.kernels.split(",") if k] or None
-    text, _ = summarize(a.stats, a.fetch, a.write, a.cmd, a.workload, kernels)
+    text, _ = summarize(a.stats, a.fetch, a.write, a.cmd, a.workload, kernels, a.counters)
     with open(a.out, "w") as f:
         f.write(text)
     print(text)
