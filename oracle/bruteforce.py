@@ -131,3 +131,48 @@ def mx_encode_line(L):
     codes = (mag | (np.signbit(blocks).astype(np.int64) << 3)).reshape(-1)
     packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
     return packed, (shared + 127).astype(np.uint8)
+
+
+# ---------------------------------------------------------- four over six
+
+def block_4o6(blk, s, err_mode: int = 0):
+    """Four-over-six step of one 16-element block by nearest-value search:
+    both candidates (amax mapped to 6, then to 4), each error summed in
+    float32 in element order, candidate 4 kept only when its error is
+    strictly smaller.  Returns (E4M3 code, 16 codes, pick)."""
+    blk = np.asarray(blk, dtype=np.float32)
+    s = F32(s)
+    b = F32(np.abs(blk).max())
+    out = []
+    for kk in (F32(6.0), F32(4.0)):
+        with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+            t = F32(0) if s == F32(0) else F32(F32(b / kk) / s)
+            S = int(e4m3_encode(np.array([t]))[0])
+            Sv = F32(E4M3[S])
+            d = F32(Sv * s)
+            m = F32(0) if d == F32(0) else F32(min(F32(F32(1.0) / d), FLT_MAX))
+            codes = e2m1_encode((blk * m).astype(np.float32))
+            e = F32(0)
+            for i in range(16):
+                q = F32(E2M1[codes[i] & 7] * (-1.0 if codes[i] & 8 else 1.0))
+                xh = F32(F32(q * Sv) * s)
+                diff = F32(blk[i] - xh)
+                e = F32(e + (F32(diff * diff) if err_mode == 0 else F32(abs(diff))))
+        out.append((S, codes, e))
+    (S6, c6, e6), (S4, c4, e4) = out
+    return (S4, c4, 4) if e4 < e6 else (S6, c6, 6)
+
+
+def encode_line_4o6(L, A, bound: int = 256, err_mode: int = 0):
+    """(packed bytes, E4M3 codes, picks) of one line, line scale A / (6 * bound)."""
+    L = np.asarray(L, dtype=np.float32)
+    s = F32(F32(A) / F32(F32(6.0) * F32(bound)))
+    S_all, codes_all, picks = [], [], []
+    for j in range(L.size // 16):
+        S, c, p = block_4o6(L[16 * j:16 * j + 16], s, err_mode)
+        S_all.append(S)
+        codes_all.append(c)
+        picks.append(p)
+    codes = np.concatenate(codes_all) if codes_all else np.zeros(0, np.int64)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    return packed, np.array(S_all, np.uint8), np.array(picks, np.uint8)

@@ -412,3 +412,147 @@ int oracle_mxfp4_group_cast(const uint16_t* x, int64_t sum_m, int64_t k, int32_t
 void oracle_mx_scale_byte_array(const float* A, int64_t n, int32_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_mx_scale_byte(A[i]);
 }
+
+/* ---------------------------------------------------------- four over six
+ *
+ * Four-over-six block scaling, the NVFP4 recipe named on the torchtitan
+ * converter page ("[NVFP4 4over6] Add the grouped-experts four-over-six
+ * converter", Summary and Review pass: recipe "four_over_six" with the knobs
+ * err_mode, e4m3_scale_bound and row_scaled).  The page gives no rule; the
+ * reading taken follows the published method it is named after ("Four Over
+ * Six: More Accurate NVFP4 Quantization with Adaptive Block Scaling"): each
+ * 16-element block is encoded twice, once with its amax mapped to 6 (the
+ * plain NVFP4 block step above) and once mapped to 4 (where the E2M1 grid is
+ * finer relative to the block's largest values), and the encoding with the
+ * smaller error is kept.  Steps, each one IEEE binary32 operation:
+ *   line scale   s = A / (6 * Bnd)       Bnd = e4m3_scale_bound, 1 .. 448
+ *   for k = 6, then k = 4:
+ *     t_k = (b / k) / s  (0 when s == 0);  S_k = E4M3(t_k);  d_k = value(S_k) * s
+ *     m_k = 1 / d_k (0 when d_k == 0, at most FLT_MAX);  c_i = E2M1(x_i * m_k)
+ *     x^_i = (value(c_i) * value(S_k)) * s        (the dequant, first product exact)
+ *     err_k = e_15 with e_{-1} = 0 and e_i = e_{i-1} + (x_i - x^_i)^2
+ *             (err_mode 0, squared error), or + |x_i - x^_i| (err_mode 1)
+ *   the block keeps k = 4 when err_4 < err_6, else k = 6.
+ * row_scaled: the line scale is per row and per column of an expert, as
+ * everywhere in this library.  With Bnd = 448 the k = 6 candidate is exactly
+ * the plain block step.  A smaller Bnd leaves room for the k = 4 scale of the
+ * line's largest block, (A/4)/s = 1.5 * Bnd, below E4M3's 448; the default
+ * taken is 256, the largest power of two with 1.5 * Bnd <= 448.
+ */
+
+float oracle_line_scale_b(float amax, int bound) {
+  return amax / (kFp4Max * (float)bound);
+}
+
+/* One candidate: scale code for divisor k, the 16 codes, and the error. */
+static int cand_4o6(const float* blk, float b, float s, float k, int err_mode,
+                    int* codes, float* err) {
+  float t = (s == 0.0f) ? 0.0f : (b / k) / s;
+  int S = oracle_e4m3_encode(t);
+  float Sv = (float)oracle_e4m3_value(S);
+  float d = Sv * s;
+  float m = 0.0f;
+  if (d != 0.0f) m = fminf(1.0f / d, FLT_MAX);
+  float e = 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    codes[i] = oracle_e2m1_encode(blk[i] * m);
+    float q = (float)oracle_e2m1_value(codes[i]);
+    float xh = (q * Sv) * s;
+    float diff = blk[i] - xh;
+    e = e + (err_mode == 0 ? diff * diff : fabsf(diff));
+  }
+  *err = e;
+  return S;
+}
+
+/* Four-over-six step for one block of 16 values on a line with scale s:
+ * writes the 16 codes, returns the scale code; *pick = 4 or 6; errs[0..1] =
+ * the errors of the k = 6 and k = 4 candidates (either may be NULL). */
+int oracle_block_4o6(const float* blk, float s, int err_mode, int* codes,
+                     int* pick, float* errs) {
+  float b = 0.0f;
+  for (int i = 0; i < 16; ++i) b = fmaxf(b, fabsf(blk[i]));
+  int c6[16], c4[16];
+  float e6, e4;
+  int S6 = cand_4o6(blk, b, s, 6.0f, err_mode, c6, &e6);
+  int S4 = cand_4o6(blk, b, s, 4.0f, err_mode, c4, &e4);
+  int use4 = e4 < e6;
+  for (int i = 0; i < 16; ++i) codes[i] = use4 ? c4[i] : c6[i];
+  if (pick) *pick = use4 ? 4 : 6;
+  if (errs) { errs[0] = e6; errs[1] = e4; }
+  return use4 ? S4 : S6;
+}
+
+static int check_4o6(int bound, int err_mode) {
+  return (bound >= 1 && bound <= 448 && (err_mode == 0 || err_mode == 1)) ? ORACLE_OK : ORACLE_EINVAL;
+}
+
+/* Encode one line (n a multiple of 16) with line amax A; picks (n/16 bytes,
+ * 4 or 6 per block) may be NULL. */
+int oracle_encode_line_4o6(const float* L, int64_t n, float A, int bound,
+                           int err_mode, uint8_t* codes, uint8_t* scales,
+                           uint8_t* picks) {
+  if (n < 0 || n % 16 != 0 || check_4o6(bound, err_mode)) return ORACLE_EINVAL;
+  float s = oracle_line_scale_b(A, bound);
+  for (int64_t j = 0; j < n / 16; ++j) {
+    int c[16], pick;
+    scales[j] = (uint8_t)oracle_block_4o6(L + 16 * j, s, err_mode, c, &pick, NULL);
+    if (picks) picks[j] = (uint8_t)pick;
+    for (int i = 0; i < 16; i += 2) codes[8 * j + i / 2] = (uint8_t)(c[i] | (c[i + 1] << 4));
+  }
+  return ORACLE_OK;
+}
+
+/* Dequantize a line encoded with line scale A / (6 * bound). */
+int oracle_decode_line_b(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                         float A, int bound, float* out) {
+  if (n < 0 || n % 16 != 0 || bound < 1 || bound > 448) return ORACLE_EINVAL;
+  float s = oracle_line_scale_b(A, bound);
+  for (int64_t i = 0; i < n; ++i) {
+    int byte = codes[i / 2];
+    int code = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+    float q = (float)oracle_e2m1_value(code);
+    float S = (float)oracle_e4m3_value(scales[i / 16]);
+    out[i] = (q * S) * s;
+  }
+  return ORACLE_OK;
+}
+
+/* Grouped four-over-six cast: the layouts, amax inputs and directions of
+ * oracle_group_cast. */
+int oracle_group_cast_4o6(const uint16_t* x, int64_t sum_m, int64_t k, int32_t E,
+                          const int64_t* splits, const float* row_amax,
+                          const float* col_amax, int bound, int err_mode,
+                          uint8_t* row_data, uint8_t* row_scale,
+                          uint8_t* col_data, uint8_t* col_scale) {
+  int rc = check_args(sum_m, k, E, splits);
+  if (rc != ORACLE_OK) return rc;
+  if (check_4o6(bound, err_mode)) return ORACLE_EINVAL;
+  int64_t cap = k > sum_m ? k : sum_m;
+  float* L = (float*)malloc(sizeof(float) * (size_t)(cap > 0 ? cap : 1));
+  if (!L) return ORACLE_EINVAL;
+  if (row_data) {
+    if (!row_scale || !row_amax) { free(L); return ORACLE_EINVAL; }
+    for (int64_t r = 0; r < sum_m; ++r) {
+      for (int64_t c = 0; c < k; ++c) L[c] = bf16_value(x[r * k + c]);
+      oracle_encode_line_4o6(L, k, row_amax[r], bound, err_mode, row_data + r * (k / 2),
+                             row_scale + r * (k / 16), NULL);
+    }
+  }
+  if (col_data) {
+    if (!col_scale || !col_amax) { free(L); return ORACLE_EINVAL; }
+    int64_t r0 = 0;
+    for (int32_t e = 0; e < E; ++e) {
+      int64_t m = splits[e];
+      for (int64_t c = 0; c < k; ++c) {
+        for (int64_t r = 0; r < m; ++r) L[r] = bf16_value(x[(r0 + r) * k + c]);
+        oracle_encode_line_4o6(L, m, col_amax[(int64_t)e * k + c], bound, err_mode,
+                               col_data + k * r0 / 2 + c * (m / 2),
+                               col_scale + k * r0 / 16 + c * (m / 16), NULL);
+      }
+      r0 += m;
+    }
+  }
+  free(L);
+  return ORACLE_OK;
+}

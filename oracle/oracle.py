@@ -79,6 +79,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_mx_decode_line.argtypes = [_P, _P, _I64, _P]
         L.oracle_mxfp4_group_cast.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P]
         L.oracle_mx_scale_byte_array.argtypes = [_P, _I64, _P]
+        L.oracle_line_scale_b.argtypes = [_F, ctypes.c_int]
+        L.oracle_line_scale_b.restype = _F
+        L.oracle_block_4o6.argtypes = [_P, _F, ctypes.c_int, _P, _P, _P]
+        L.oracle_block_4o6.restype = ctypes.c_int
+        L.oracle_encode_line_4o6.argtypes = [_P, _I64, _F, ctypes.c_int, ctypes.c_int, _P, _P, _P]
+        L.oracle_decode_line_b.argtypes = [_P, _P, _I64, _F, ctypes.c_int, _P]
+        L.oracle_group_cast_4o6.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, ctypes.c_int, ctypes.c_int,
+                                            _P, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -282,6 +290,77 @@ def mxfp4_group_cast(x: np.ndarray, splits, rowwise: bool = True, columnwise: bo
     _check(lib().oracle_mxfp4_group_cast(_ptr(x), sum_m, k, sp.size, _ptr(sp), _ptr(rd), _ptr(rs), _ptr(cd),
                                          _ptr(cs)), "mxfp4_group_cast")
     return rd, rs, cd, cs
+
+
+# ---------------------------------------------------------- four over six
+#
+# The four-over-six block scaling of nvfp4_oracle.c (each block encoded with
+# its amax mapped to 6 and to 4, the smaller error kept; line scale
+# A / (6 * bound)).
+
+DEFAULT_4O6_BOUND = 256
+ERR_MSE, ERR_MAE = 0, 1
+
+
+def line_scale_b(amax: float, bound: int) -> np.float32:
+    return np.float32(lib().oracle_line_scale_b(float(amax), int(bound)))
+
+
+def block_4o6(blk, s: float, err_mode: int = ERR_MSE):
+    """One 16-element block: (E4M3 code, 16 codes, pick 4 or 6, (err_6, err_4))."""
+    blk = np.ascontiguousarray(blk, dtype=np.float32)
+    assert blk.size == 16
+    codes = np.empty(16, dtype=np.int32)
+    pick = ctypes.c_int()
+    errs = np.empty(2, dtype=np.float32)
+    S = lib().oracle_block_4o6(_ptr(blk), float(s), int(err_mode), _ptr(codes), ctypes.byref(pick), _ptr(errs))
+    return S, codes, pick.value, (errs[0], errs[1])
+
+
+def encode_line_4o6(L, amax: float, bound: int = DEFAULT_4O6_BOUND, err_mode: int = ERR_MSE):
+    """(packed codes, E4M3 scales, picks) of one line."""
+    L = np.ascontiguousarray(L, dtype=np.float32)
+    n = L.size
+    codes = np.empty(n // 2, dtype=np.uint8)
+    scales = np.empty(n // 16, dtype=np.uint8)
+    picks = np.empty(n // 16, dtype=np.uint8)
+    _check(lib().oracle_encode_line_4o6(_ptr(L), n, float(amax), int(bound), int(err_mode), _ptr(codes),
+                                        _ptr(scales), _ptr(picks)), "encode_line_4o6")
+    return codes, scales, picks
+
+
+def decode_line_b(codes, scales, n: int, amax: float, bound: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty(n, dtype=np.float32)
+    _check(lib().oracle_decode_line_b(_ptr(codes), _ptr(scales), n, float(amax), int(bound), _ptr(out)),
+           "decode_line_b")
+    return out
+
+
+def group_cast_4o6(x: np.ndarray, splits, row_amax=None, col_amax=None, bound: int = DEFAULT_4O6_BOUND,
+                   err_mode: int = ERR_MSE, rowwise: bool = True, columnwise: bool = True):
+    """Grouped four-over-six cast: (row_data, row_scale, col_data, col_scale)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    sum_m, k = x.shape
+    sp = np.ascontiguousarray(splits, dtype=np.int64)
+    rd = np.empty((sum_m, k // 2), dtype=np.uint8) if rowwise else None
+    rs = np.empty((sum_m, k // 16), dtype=np.uint8) if rowwise else None
+    cd = np.empty(sum_m * k // 2, dtype=np.uint8) if columnwise else None
+    cs = np.empty(sum_m * k // 16, dtype=np.uint8) if columnwise else None
+    ra = None if row_amax is None else np.ascontiguousarray(row_amax, dtype=np.float32)
+    ca = None if col_amax is None else np.ascontiguousarray(col_amax, dtype=np.float32)
+    _check(lib().oracle_group_cast_4o6(_ptr(x), sum_m, k, sp.size, _ptr(sp), _ptr(ra), _ptr(ca), int(bound),
+                                       int(err_mode), _ptr(rd), _ptr(rs), _ptr(cd), _ptr(cs)), "group_cast_4o6")
+    return rd, rs, cd, cs
+
+
+def group_quantize_4o6(x: np.ndarray, splits, bound: int = DEFAULT_4O6_BOUND, err_mode: int = ERR_MSE,
+                       rowwise: bool = True, columnwise: bool = True):
+    """Amax (the plain grouped amax) then the four-over-six cast."""
+    ra, ca = group_amax(x, splits, rowwise, columnwise)
+    rd, rs, cd, cs = group_cast_4o6(x, splits, ra, ca, bound, err_mode, rowwise, columnwise)
+    return {"row_amax": ra, "col_amax": ca, "row_data": rd, "row_scale": rs, "col_data": cd, "col_scale": cs}
 
 
 # ------------------------------------------------- row-scaled grouped GEMM

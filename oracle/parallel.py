@@ -79,11 +79,18 @@ def alloc(sum_m: int, k: int, num_experts: int, rowwise: bool, columnwise: bool)
     return res
 
 
-def run_task(x: np.ndarray, k: int, task, res: dict) -> None:
+def _call(x, splits, rowwise, columnwise, four_over_six):
+    if four_over_six is None:
+        return O.group_quantize(x, splits, rowwise, columnwise)
+    bound, err_mode = four_over_six
+    return O.group_quantize_4o6(x, splits, bound, err_mode, rowwise, columnwise)
+
+
+def run_task(x: np.ndarray, k: int, task, res: dict, four_over_six=None) -> None:
     """One oracle call; its bytes go to their place in the whole outputs."""
     if task[0] == "row":
         _, r0, r1 = task
-        part = O.group_quantize(x[r0:r1], [r1 - r0], True, False)
+        part = _call(x[r0:r1], [r1 - r0], True, False, four_over_six)
         res["row_amax"][r0:r1] = part["row_amax"]
         res["row_data"][r0:r1] = part["row_data"]
         res["row_scale"][r0:r1] = part["row_scale"]
@@ -91,7 +98,7 @@ def run_task(x: np.ndarray, k: int, task, res: dict) -> None:
         _, e, lo, hi, c0, c1 = task
         m = hi - lo
         xs = np.ascontiguousarray(x[lo:hi, c0:c1])
-        part = O.group_quantize(xs, [m], False, True)
+        part = _call(xs, [m], False, True, four_over_six)
         res["col_amax"][e * k + c0:e * k + c1] = part["col_amax"]
         res["col_data"][k * lo // 2 + c0 * (m // 2):k * lo // 2 + c1 * (m // 2)] = part["col_data"]
         res["col_scale"][k * lo // 16 + c0 * (m // 16):k * lo // 16 + c1 * (m // 16)] = part["col_scale"]
@@ -99,10 +106,12 @@ def run_task(x: np.ndarray, k: int, task, res: dict) -> None:
 
 def group_quantize(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool = True,
                    threads: int | None = None, rows_per_task: int = ROWS_PER_TASK,
-                   cols_per_task: int = COLS_PER_TASK) -> dict:
+                   cols_per_task: int = COLS_PER_TASK, four_over_six=None) -> dict:
     """The oracle's amax + cast of the whole packed buffer ``x`` (bf16 bits,
     (sum_m, k)), as one dict of numpy arrays (None for a direction not asked
-    for)."""
+    for).  ``four_over_six = (bound, err_mode)`` runs the oracle's
+    four-over-six cast instead of the plain one (the pieces are independent
+    in the same way: a block's choice depends only on its line)."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     sum_m, k = x.shape
     sp = [int(v) for v in splits]
@@ -113,9 +122,9 @@ def group_quantize(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool
     n = threads or default_threads()
     if n == 1:
         for t in work:
-            run_task(x, k, t, res)
+            run_task(x, k, t, res, four_over_six)
     else:
         with ThreadPoolExecutor(max_workers=n) as pool:
-            for f in [pool.submit(run_task, x, k, t, res) for t in work]:
+            for f in [pool.submit(run_task, x, k, t, res, four_over_six) for t in work]:
                 f.result()
     return res

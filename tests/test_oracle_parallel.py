@@ -41,3 +41,16 @@ def test_tasks_cover_every_row_and_column_once():
 
 def test_default_threads_bounded():
     assert 1 <= OP.default_threads() <= OP.MAX_THREADS
+
+
+@pytest.mark.parametrize("bound,mode", [(256, 0), (448, 1)])
+def test_parallel_four_over_six_equals_one_call(bound, mode):
+    w = synth.random_case(23, [256, 0, 384, 128], 96, "rowscale")
+    ref = O.group_quantize_4o6(w.x, w.splits, bound, mode)
+    got = OP.group_quantize(w.x, w.splits, threads=3, rows_per_task=128, cols_per_task=32,
+                            four_over_six=(bound, mode))
+    for key in KEYS:
+        a, b = np.asarray(got[key]), np.asarray(ref[key])
+        if a.dtype == np.float32:
+            a, b = a.view(np.uint32), b.view(np.uint32)
+        assert np.array_equal(a.reshape(-1), b.reshape(-1)), key
