@@ -33,7 +33,8 @@ Beside the headline the line carries:
   ratio in a contiguous layout, and the cast's own memory pattern with the
   arithmetic removed) and torch's device copy;
 - ``next_rows``: the grouped MXFP4 cast of the same input, the rowwise /
-  columnwise NVFP4 dequant of the step's outputs, and the row-scaled grouped
+  columnwise NVFP4 dequant of the step's outputs, the four-over-six cast of
+  the same input (vector-ALU-bound), and the row-scaled grouped
   GEMM (forward and weight gradient, MFMA-bound, TFLOP/s against the fp16
   MFMA peak) with torch.matmul (hipBLASLt) fp16 on the same shapes beside it;
 - ``cpu_baseline``: the CPU oracle over the whole workload on the host's
@@ -531,7 +532,39 @@ def next_rows(B, torch, tev, x, splits, out, E: int, k: int, m: int, reps: int) 
                                                          splits, k, deq))
     res["nvfp4_group_dequant_columnwise"] = entry("dequant_kernel", ms, N // 2 + N // 16 + 4 * E * k + 4 * N)
     del deq
+    res.update(four_over_six_rows(B, torch, timed, entry, x, splits, out, E, k, m))
     res.update(gemm_rows(B, torch, timed, out, splits, E, k, m))
+    return res
+
+
+# fp32 operations the four-over-six method performs per element, direction
+# and candidate: x*m, value(code)*value(S), *s, the difference, its square
+# (or absolute value) and the running sum
+FOUR_OVER_SIX_OPS = 6
+# non-packed fp32 VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_LANE_OPS_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def four_over_six_rows(B, torch, timed, entry, x, splits, out, E: int, k: int, m: int) -> dict:
+    """The four-over-six cast of the step's input (both directions, default
+    bound 256, squared and absolute error), consuming the step's amax.  The
+    kernel is bound by the vector ALUs: beside the HBM figures it reports the
+    method's fp32 operations per second against the non-packed VALU rate."""
+    print("[bench] four-over-six cast", file=sys.stderr, flush=True)
+    N = m * k
+    res = {}
+    o = B.alloc_outputs(m, k, E, device=x.device)
+    o["row_amax"], o["col_amax"] = out["row_amax"], out["col_amax"]
+    for mode, tag in ((B.ERR_MSE, "mse"), (B.ERR_MAE, "mae")):
+        ms = timed(lambda: B.nvfp4_group_cast_4over6(x, splits, **o, scale_bound=B.DEFAULT_4O6_BOUND,
+                                                      err_mode=mode))
+        r = entry("group_cast_4o6_kernel", ms, 2 * N + 2 * (N // 2 + N // 16) + 4 * m + 4 * E * k)
+        ops = 2 * 2 * FOUR_OVER_SIX_OPS * N
+        r["alu"] = {"bound": "alu", "method_fp32_ops_per_launch": ops,
+                    "achieved_Tops": round(ops / (ms * 1e-3) / 1e12, 2), "peak_Tops": VALU_LANE_OPS_PEAK_T,
+                    "frac": round(ops / (ms * 1e-3) / 1e12 / VALU_LANE_OPS_PEAK_T, 4)}
+        res[f"nvfp4_group_cast_4over6_{tag}"] = r
+    del o
     return res
 
 

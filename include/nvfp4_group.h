@@ -294,6 +294,53 @@ int nvfp4_group_gemm_wgrad_graphsafe(const uint8_t* a_col_data,
                                      const int32_t* d_offs, float* out,
                                      int32_t* d_status, void* stream);
 
+/* Grouped cast with four-over-six block scaling: the "four_over_six" NVFP4
+ * recipe named on the torchtitan converter page ("[NVFP4 4over6] Add the
+ * grouped-experts four-over-six converter", Summary and Review pass: knobs
+ * err_mode, e4m3_scale_bound, row_scaled).  The page does not state the
+ * block rule; the one implemented is that of the published method of the
+ * same name ("Four Over Six: More Accurate NVFP4 Quantization with Adaptive
+ * Block Scaling"), as a reading, not as a page fact.  Per line with amax A
+ * and per 16-element block with block amax b, each step one IEEE binary32
+ * operation (round to nearest even, no FMA contraction, denormals kept):
+ *     s = A / (6 * scale_bound)
+ *     for k = 6 and k = 4:
+ *       t_k = (b / k) / s (0 when s == 0);  S_k = E4M3FN(t_k) (as above)
+ *       d_k = value(S_k) * s;  m_k = 1 / d_k (0 when d_k == 0, <= FLT_MAX)
+ *       c_i = E2M1(x_i * m_k);  x^_i = (value(c_i) * value(S_k)) * s
+ *       err_k = (...((0 + r_0) + r_1) + ... ) + r_15, element order, with
+ *               r_i = (x_i - x^_i)^2 (err_mode 0) or |x_i - x^_i| (1)
+ *     the block keeps k = 4 (codes and scale) when err_4 < err_6, else k = 6.
+ * Dequantisation: (value(code) * value(S)) * (A / (6 * scale_bound)).  With
+ * scale_bound = 448 the k = 6 candidate is the plain cast's block step.
+ * scale_bound: 1 .. NVFP4G_4O6_MAX_BOUND; err_mode: NVFP4G_4O6_ERR_MSE or
+ * NVFP4G_4O6_ERR_MAE; anything else returns NVFP4G_EINVAL.  Amax inputs
+ * (from nvfp4_group_amax), layouts, directions and the other arguments as
+ * in nvfp4_group_cast.  x must be finite. */
+#define NVFP4G_4O6_ERR_MSE 0
+#define NVFP4G_4O6_ERR_MAE 1
+#define NVFP4G_4O6_MAX_BOUND 448
+#define NVFP4G_4O6_DEFAULT_BOUND 256 /* largest power of two with 1.5 * bound <= 448 */
+int nvfp4_group_cast_4over6(const uint16_t* x, int64_t sum_m, int64_t k,
+                            int32_t num_experts, const int64_t* h_splits,
+                            const float* row_amax, const float* col_amax,
+                            int32_t scale_bound, int32_t err_mode,
+                            uint8_t* row_data, uint8_t* row_scale,
+                            uint8_t* col_data, uint8_t* col_scale, void* stream);
+
+/* Graph-safe form of nvfp4_group_cast_4over6: routing from d_offs, buffers
+ * and status as in nvfp4_group_cast_graphsafe; output bytes equal those of
+ * nvfp4_group_cast_4over6 for the same routing. */
+int nvfp4_group_cast_4over6_graphsafe(const uint16_t* x, int64_t m_capacity,
+                                      int64_t k, int32_t num_experts,
+                                      const int32_t* d_offs,
+                                      const float* row_amax,
+                                      const float* col_amax,
+                                      int32_t scale_bound, int32_t err_mode,
+                                      uint8_t* row_data, uint8_t* row_scale,
+                                      uint8_t* col_data, uint8_t* col_scale,
+                                      int32_t* d_status, void* stream);
+
 /* Static description of a status code. */
 const char* nvfp4_group_strerror(int status);
 

@@ -41,8 +41,16 @@ EXPORTS = (
     "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
     "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
     "nvfp4_group_gemm", "nvfp4_group_gemm_graphsafe", "nvfp4_group_gemm_wgrad", "nvfp4_group_gemm_wgrad_graphsafe",
+    "nvfp4_group_cast_4over6", "nvfp4_group_cast_4over6_graphsafe",
     "nvfp4_group_strerror",
 )
+
+# four-over-six knobs (nvfp4_group_cast_4over6): error modes and the
+# e4m3_scale_bound range / default
+ERR_MSE = 0
+ERR_MAE = 1
+MAX_4O6_BOUND = 448
+DEFAULT_4O6_BOUND = 256
 
 
 class Nvfp4GroupError(RuntimeError):
@@ -79,6 +87,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.nvfp4_group_gemm_graphsafe.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P]
     L.nvfp4_group_gemm_wgrad.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P]
     L.nvfp4_group_gemm_wgrad_graphsafe.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P]
+    L.nvfp4_group_cast_4over6.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P]
+    L.nvfp4_group_cast_4over6_graphsafe.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _P,
+                                                    _P, _P]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = ctypes.c_int
     L.nvfp4_group_strerror.argtypes = [ctypes.c_int]
@@ -228,6 +239,27 @@ def nvfp4_group_quantize_graphsafe(x, num_experts, d_offs, d_status, row_amax=No
     bufs = _outputs(m, k, e, row_amax, col_amax, row_data, row_scale, col_data, col_scale)
     _check("nvfp4_group_quantize_graphsafe", load_library().nvfp4_group_quantize_graphsafe(
         xp, m, k, e, do, *bufs, ds, _stream(stream)))
+
+
+def nvfp4_group_cast_4over6(x, h_splits, row_amax=None, col_amax=None, row_data=None, row_scale=None,
+                            col_data=None, col_scale=None, scale_bound=DEFAULT_4O6_BOUND, err_mode=ERR_MSE,
+                            stream=None):
+    xp, m, k = _x(x)
+    sp, e = _splits(h_splits)
+    ra, ca, rd, rs, cd, cs = _outputs(m, k, e, row_amax, col_amax, row_data, row_scale, col_data, col_scale)
+    _check("nvfp4_group_cast_4over6", load_library().nvfp4_group_cast_4over6(
+        xp, m, k, e, sp, ra, ca, int(scale_bound), int(err_mode), rd, rs, cd, cs, _stream(stream)))
+
+
+def nvfp4_group_cast_4over6_graphsafe(x, num_experts, d_offs, d_status, row_amax=None, col_amax=None,
+                                      row_data=None, row_scale=None, col_data=None, col_scale=None,
+                                      scale_bound=DEFAULT_4O6_BOUND, err_mode=ERR_MSE, stream=None):
+    xp, m, k = _x(x)
+    e = int(num_experts)
+    do, ds = _routing(e, d_offs, d_status)
+    ra, ca, rd, rs, cd, cs = _outputs(m, k, e, row_amax, col_amax, row_data, row_scale, col_data, col_scale)
+    _check("nvfp4_group_cast_4over6_graphsafe", load_library().nvfp4_group_cast_4over6_graphsafe(
+        xp, m, k, e, do, ra, ca, int(scale_bound), int(err_mode), rd, rs, cd, cs, ds, _stream(stream)))
 
 
 def nvfp4_group_dequant_rowwise(row_data, row_scale, row_amax, out, stream=None):

@@ -150,6 +150,63 @@ __device__ __forceinline__ void load_tile(const uint16_t* tile, uint32_t ku, uin
   }
 }
 
+// --------------------------------------------------- staged tile outputs
+
+// The NVFP4 cast kernels stage a tile's rowwise codes and both directions'
+// scales in LDS and write them after a barrier.  Rowwise codes: 128 rows x
+// 128 bytes; the lane holding rows 16*rb.. and columns 8*cg.. of wave w
+// writes dword 8*w + cg of a row, at slot (8*w + cg) ^ (4*rb): the 16-byte
+// granule q of row r sits at granule slot q ^ ((r / 16) % 8), so the 4-byte
+// writes of a wave (lanes on eight rows 16 apart, same dword column) fall in
+// distinct banks.  Scales: 16 bytes per row, 8 per column (one per 16-row
+// block).
+typedef uint32_t StagedRowData[kTileRows][kTileCols / 8];
+typedef uint32_t StagedRowScales[kTileRows][kTileCols / 64];
+typedef uint32_t StagedColScales[kTileCols][2];
+
+__device__ __forceinline__ uint32_t row_slot(int rb, int wave, int cg) { return (uint32_t)((8 * wave + cg) ^ (rb << 2)); }
+
+// Writes a staged 128 x 256 tile (ncols <= 256 valid columns from col_base,
+// rows row0.. of the expert owning rows [rbeg, rbeg + me)): whole 128-byte
+// row lines, 16 bytes per thread (thread t: granule t % 8 of rows t / 8 +
+// 32 * it; a granule of a ragged last chunk may hold only 16 valid columns),
+// one 16-byte row-scale piece per row and one 8-byte column-scale piece per
+// column.  row_data == nullptr skips the rowwise output, col_scale ==
+// nullptr the column scales.
+__device__ __forceinline__ void store_staged_tile(const StagedRowData& l_rd, const StagedRowScales& l_rs,
+                                                  const StagedColScales& l_cs, int64_t k, int32_t row0,
+                                                  int64_t col_base, uint32_t ncols, int32_t rbeg, uint32_t me,
+                                                  uint8_t* row_data, uint8_t* row_scale, uint8_t* col_scale) {
+  const int tid = threadIdx.x;
+  const uint32_t ku = (uint32_t)k;
+  if (row_data) {
+    const rsrc_t rd = make_rsrc(row_data + (int64_t)row0 * (k / 2) + col_base / 2);
+    const uint32_t g = tid & 7;
+#pragma unroll
+    for (int it = 0; it < kTileRows / 32; ++it) {
+      const uint32_t r = 32 * it + (tid >> 3);
+      const u32x4 q = *reinterpret_cast<const u32x4*>(&l_rd[r][4 * (g ^ ((r >> 4) & 7))]);
+      if (32 * g + 32 <= ncols)
+        __builtin_amdgcn_raw_buffer_store_b128(q, rd, r * (ku / 2) + 16 * g, 0, kStoreAux);
+      else if (32 * g < ncols)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, rd, r * (ku / 2) + 16 * g, 0, kStoreAux);
+    }
+  }
+  if (row_data && tid < kTileRows) {
+    uint8_t* dst = row_scale + ((int64_t)row0 + tid) * (k / 16) + col_base / 16;
+    if (ncols == kTileCols && (k & 255) == 0) {
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&l_rs[tid][0]);
+    } else {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(&l_rs[tid][0]);
+      for (uint32_t b = 0; b < ncols / 16; ++b) dst[b] = src[b];
+    }
+  }
+  if (col_scale && (uint32_t)tid < ncols) {
+    uint8_t* dst = col_scale + k * (int64_t)rbeg / 16 + (col_base + tid) * (int64_t)(me / 16) + (row0 - rbeg) / 16;
+    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&l_cs[tid][0]);
+  }
+}
+
 // ------------------------------------------------------------- host side
 
 constexpr int64_t kMaxK = NVFP4G_MAX_K;
@@ -195,6 +252,18 @@ inline int graph_routing(const int32_t* d_offs, int32_t* d_status, int32_t E, in
   if (!aligned(d_offs, 4) || !aligned(d_status, 4)) return NVFP4G_EALIGN;
   R->d_offs = d_offs;
   R->d_status = d_status;
+  return NVFP4G_OK;
+}
+
+// Outputs of a cast: a direction is produced when its data pointer is set,
+// and then needs its scales and amax.
+inline int check_cast_outputs(const float* row_amax, const float* col_amax, const uint8_t* row_data,
+                              const uint8_t* row_scale, const uint8_t* col_data, const uint8_t* col_scale) {
+  if (row_data && (!row_scale || !row_amax)) return NVFP4G_EINVAL;
+  if (col_data && (!col_scale || !col_amax)) return NVFP4G_EINVAL;
+  if (!aligned(row_data, 16) || !aligned(row_scale, 16) || !aligned(col_data, 16) ||
+      !aligned(col_scale, 16) || !aligned(row_amax, 4) || !aligned(col_amax, 4))
+    return NVFP4G_EALIGN;
   return NVFP4G_OK;
 }
 

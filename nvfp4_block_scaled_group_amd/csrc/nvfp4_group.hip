@@ -340,9 +340,9 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
     uint8_t* __restrict__ col_data, uint8_t* __restrict__ col_scale) {
   __shared__ float2 l_row[kTileRows];                   // (s, 1/s) per row of the tile
   __shared__ float2 l_col[kTileCols];                   // (s, 1/s) per column of the tile
-  __shared__ uint32_t l_rs[kTileRows][kTileCols / 64];  // row scales, 16 per row
-  __shared__ uint32_t l_cs[kTileCols][2];               // column scales, 8 per column
-  __shared__ uint32_t l_rd[kTileRows][kTileCols / 8];   // row data, 128 bytes per row (swizzled)
+  __shared__ StagedRowScales l_rs;
+  __shared__ StagedColScales l_cs;
+  __shared__ StagedRowData l_rd;
   __shared__ uint32_t l_slow[kThreads / 64];            // per wave: a line needs the exact block step
   if (!routing_ok(R)) return;
   const int32_t total = route_end(R, R.num_experts - 1);
@@ -420,13 +420,13 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
           packed = FP4X2(packed, bf16lo(v[i][1]) * m_lo, bf16hi(v[i][1]) * m_lo, 1);
           packed = FP4X2(packed, bf16lo(v[i][2]) * m_lo, bf16hi(v[i][2]) * m_lo, 2);
           packed = FP4X2(packed, bf16lo(v[i][3]) * m_lo, bf16hi(v[i][3]) * m_lo, 3);
-          l_rd[16 * rb + i][(8 * wave + cg) ^ (rb << 2)] = packed;
+          l_rd[16 * rb + i][row_slot(rb, wave, cg)] = packed;
           packed = 0;
           packed = FP4X2(packed, bf16lo(v[8 + i][0]) * m_hi, bf16hi(v[8 + i][0]) * m_hi, 0);
           packed = FP4X2(packed, bf16lo(v[8 + i][1]) * m_hi, bf16hi(v[8 + i][1]) * m_hi, 1);
           packed = FP4X2(packed, bf16lo(v[8 + i][2]) * m_hi, bf16hi(v[8 + i][2]) * m_hi, 2);
           packed = FP4X2(packed, bf16lo(v[8 + i][3]) * m_hi, bf16hi(v[8 + i][3]) * m_hi, 3);
-          l_rd[16 * rb + 8 + i][(8 * wave + cg) ^ (rb << 2)] = packed;
+          l_rd[16 * rb + 8 + i][row_slot(rb, wave, cg)] = packed;
         }
       }
 
@@ -464,36 +464,9 @@ __global__ __launch_bounds__(kThreads) void group_cast_kernel(
     else
       encode(BoolTag<false>{});
 
-    // rowwise data and scales: staged in LDS, then wide stores per line
     __syncthreads();
-    if (row_data) {
-      // thread t writes granule t % 8 (32 columns) of rows t / 8 + 32 * it;
-      // a granule of a ragged last chunk may hold only 16 valid columns
-      const rsrc_t rd = make_rsrc(row_data + (int64_t)row0 * (k / 2) + col_base / 2);
-      const uint32_t g = tid & 7;
-#pragma unroll
-      for (int it = 0; it < kTileRows / 32; ++it) {
-        const uint32_t r = 32 * it + (tid >> 3);
-        const u32x4 q = *reinterpret_cast<const u32x4*>(&l_rd[r][4 * (g ^ ((r >> 4) & 7))]);
-        if (32 * g + 32 <= ncols)
-          __builtin_amdgcn_raw_buffer_store_b128(q, rd, r * (ku / 2) + 16 * g, 0, kStoreAux);
-        else if (32 * g < ncols)
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, rd, r * (ku / 2) + 16 * g, 0, kStoreAux);
-      }
-    }
-    if (row_data && tid < kTileRows) {
-      uint8_t* dst = row_scale + ((int64_t)row0 + tid) * (k / 16) + col_base / 16;
-      if (ncols == kTileCols && (k & 255) == 0) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&l_rs[tid][0]);
-      } else {
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(&l_rs[tid][0]);
-        for (uint32_t b = 0; b < ncols / 16; ++b) dst[b] = src[b];
-      }
-    }
-    if (col_data && (uint32_t)tid < ncols) {
-      uint8_t* dst = col_scale + k * (int64_t)rbeg / 16 + (col_base + tid) * (int64_t)(me / 16) + (row0 - rbeg) / 16;
-      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&l_cs[tid][0]);
-    }
+    store_staged_tile(l_rd, l_rs, l_cs, k, row0, col_base, ncols, rbeg, me, row_data, row_scale,
+                      col_data ? col_scale : nullptr);
   }
 }
 
@@ -744,16 +717,6 @@ __global__ __launch_bounds__(kSmallThreads) void group_quantize_small_kernel(
 }
 
 // ------------------------------------------------------------- host side
-
-int check_cast_outputs(const float* row_amax, const float* col_amax, const uint8_t* row_data,
-                       const uint8_t* row_scale, const uint8_t* col_data, const uint8_t* col_scale) {
-  if (row_data && (!row_scale || !row_amax)) return NVFP4G_EINVAL;
-  if (col_data && (!col_scale || !col_amax)) return NVFP4G_EINVAL;
-  if (!aligned(row_data, 16) || !aligned(row_scale, 16) || !aligned(col_data, 16) ||
-      !aligned(col_scale, 16) || !aligned(row_amax, 4) || !aligned(col_amax, 4))
-    return NVFP4G_EALIGN;
-  return NVFP4G_OK;
-}
 
 // Persistent amax grid: enough resident workgroups to cover the device
 // (at most the number of 64 x 512 tiles of the buffers).

@@ -9,6 +9,8 @@
 //  * the kernels' block step (fast path for line scales >= 2^-112, IEEE
 //    divisions below) against the IEEE-division block step on every pair of
 //    bf16 values b <= A (b = block amax, A = line amax);
+//  * the hardware FP4 -> fp32 convert with unit scale (the four-over-six
+//    cast's dequantised values) on every byte at every byte position;
 //  * sample outputs (block step, FP4 codes) that the tests compare with the
 //    CPU oracle.
 #include <hip/hip_runtime.h>
@@ -106,6 +108,24 @@ __global__ void fp4_codes_kernel(const float* v, int64_t n, uint8_t* codes) {
   codes[i] = (uint8_t)(FP4X2(0u, v[i], 0.0f, 0) & 0xFu);
 }
 
+// out[2 * (4 * byte + sel) + h]: nibble h of `byte` placed at byte position
+// sel of a word whose other bytes are 0x5A, decoded with unit scale.
+__global__ void fp4_decode_kernel(float* out) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;  // 0 .. 1023
+  if (t >= 1024) return;
+  const uint32_t byte = t >> 2, sel = t & 3;
+  const uint32_t w = (0x5A5A5A5Au & ~(0xFFu << (8 * sel))) | (byte << (8 * sel));
+  float lo, hi;
+  switch (sel) {
+    case 0: { const auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); lo = q[0]; hi = q[1]; break; }
+    case 1: { const auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); lo = q[0]; hi = q[1]; break; }
+    case 2: { const auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); lo = q[0]; hi = q[1]; break; }
+    default: { const auto q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); lo = q[0]; hi = q[1]; break; }
+  }
+  out[2 * t] = lo;
+  out[2 * t + 1] = hi;
+}
+
 int status() { return hipGetLastError() == hipSuccess ? 0 : -4; }
 
 }  // namespace
@@ -144,6 +164,12 @@ int selftest_block_step_sample(const uint16_t* b16, const uint16_t* A16, int64_t
 int selftest_fp4_codes(const float* v, int64_t n, uint8_t* codes) {
   if (n <= 0) return 0;
   hipLaunchKernelGGL(fp4_codes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, 0, v, n, codes);
+  return status();
+}
+
+// out: device fp32[2048] (see fp4_decode_kernel).
+int selftest_fp4_decode(float* out) {
+  hipLaunchKernelGGL(fp4_decode_kernel, dim3(4), dim3(256), 0, 0, out);
   return status();
 }
 

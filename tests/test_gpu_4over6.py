@@ -1,0 +1,205 @@
+"""Parity of the four-over-six grouped cast (HIP, through the C ABI) with the
+CPU oracle's four-over-six cast, element by element and bit-exact: small and
+ragged shapes for every error mode and several scale bounds, each direction
+alone, the graph-safe form under partial routing and under graph replay with
+changed routing, and the two full-size expert workloads on every byte.
+
+The amax comes from the library's grouped amax (checked equal to the
+oracle's); the four-over-six cast consumes it."""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_block_scaled_group_amd import binding as B
+from nvfp4_block_scaled_group_amd import synth
+from oracle import oracle as O
+from oracle import parallel as OP
+
+from gpu_helpers import alloc, assert_equal_outputs, assert_guards, log, tensors, to_device, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+KNOBS = [(256, B.ERR_MSE), (448, B.ERR_MAE), (100, B.ERR_MSE), (1, B.ERR_MAE), (448, B.ERR_MSE), (37, B.ERR_MAE)]
+
+
+def run_4o6(x_dev, splits, bound, mode, rowwise=True, columnwise=True):
+    m, k = x_dev.shape
+    out = alloc(m, k, len(splits), rowwise, columnwise)
+    t = tensors(out)
+    B.nvfp4_group_amax(x_dev, splits, t["row_amax"], t["col_amax"])
+    B.nvfp4_group_cast_4over6(x_dev, splits, **t, scale_bound=bound, err_mode=mode)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(w, bound, mode, rowwise=True, columnwise=True):
+    splits = list(map(int, w.splits))
+    log(f"4over6 {w.name} m={w.sum_m} k={w.k} splits={splits} bound={bound} mode={mode} "
+        f"row={rowwise} col={columnwise}")
+    out = run_4o6(to_device(w.x), splits, bound, mode, rowwise, columnwise)
+    assert_guards(out)
+    gpu = to_numpy(out)
+    ref = O.group_quantize_4o6(w.x, splits, bound, mode, rowwise, columnwise)
+    assert_equal_outputs(gpu, ref)
+    return gpu, ref
+
+
+SMALL = [
+    ([128, 0, 256, 128], 272, "normal", 31),       # 272 = 256 + 16: ragged column chunk
+    ([384, 128], 48, "outliers", 32),
+    ([256, 256, 0, 0, 512], 784, "outliers", 33),  # 784 = 3*256 + 16
+    ([128, 128, 128], 16, "sparse", 34),           # all-zero blocks and rows
+    ([640, 128], 2064, "rowscale", 35),
+    ([0, 256, 128, 0], 512, "student", 36),        # gradient-like small values
+    ([128] * 9, 96, "normal", 37),
+]
+
+
+@pytest.mark.parametrize("knob", range(len(KNOBS)))
+def test_tiny_config_every_knob(knob):
+    bound, mode = KNOBS[knob]
+    check(synth.tiny(), bound, mode)
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_ragged_cases(case):
+    splits, k, dist, seed = SMALL[case]
+    w = synth.random_case(seed, splits, k, dist)
+    for bound, mode in (KNOBS[case % len(KNOBS)], KNOBS[(case + 3) % len(KNOBS)]):
+        check(w, bound, mode)
+
+
+@pytest.mark.parametrize("rowwise,columnwise", [(True, False), (False, True)])
+def test_one_direction(rowwise, columnwise):
+    w = synth.random_case(41, [256, 128, 0, 384], 1040, "normal")
+    check(w, 256, B.ERR_MSE, rowwise, columnwise)
+
+
+def test_both_candidates_are_taken():
+    """The parity above is only meaningful if blocks pick both encodings: on
+    the normal workload about half of the blocks keep k = 4; with bound 448
+    the k = 6 candidate is the plain cast's, so the blocks whose scale byte
+    differs from the plain cast are exactly the k = 4 picks."""
+    w = synth.random_case(42, [256, 256], 512, "normal")
+    gpu, _ = check(w, 448, B.ERR_MSE)
+    plain = O.group_quantize(w.x, list(map(int, w.splits)))
+    frac_row = float((gpu["row_scale"] != plain["row_scale"]).mean())
+    frac_col = float((gpu["col_scale"] != plain["col_scale"]).mean())
+    log(f"blocks taking k = 4: rowwise {frac_row:.3f}, columnwise {frac_col:.3f}")
+    assert 0.1 < frac_row < 0.9 and 0.1 < frac_col < 0.9
+
+
+def test_graphsafe_partial_routing_leaves_the_tail_untouched():
+    """Capacity 1024 rows, routed 640: the routed rows equal the oracle's
+    four-over-six cast of those rows, and nothing at or beyond the routed
+    total is written."""
+    k, cap, splits = 1040, 1024, [256, 0, 384]
+    w = synth.random_case(43, [cap], k, "normal")
+    x_dev = to_device(w.x)
+    routed = sum(splits)
+    offs = torch.tensor(B.offsets_from_splits(splits), dtype=torch.int32, device="cuda:0")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    out = alloc(cap, k, len(splits), True, True)
+    for g in out.values():
+        g.t.view(torch.uint8).fill_(0x5A)
+    t = tensors(out)
+    log(f"4over6 graphsafe partial routing cap={cap} routed={routed} k={k}")
+    B.nvfp4_group_amax_graphsafe(x_dev, len(splits), offs, status, t["row_amax"], t["col_amax"])
+    B.nvfp4_group_cast_4over6_graphsafe(x_dev, len(splits), offs, status, **t, scale_bound=256,
+                                        err_mode=B.ERR_MSE)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert_guards(out)
+    gpu = {key: g.numpy() for key, g in out.items()}
+    ref = O.group_quantize_4o6(w.x[:routed], splits, 256, B.ERR_MSE)
+    assert np.array_equal(gpu["row_data"][:routed], ref["row_data"])
+    assert np.array_equal(gpu["row_scale"][:routed], ref["row_scale"])
+    assert np.array_equal(gpu["col_data"][:k * routed // 2], ref["col_data"])
+    assert np.array_equal(gpu["col_scale"][:k * routed // 16], ref["col_scale"])
+    assert (gpu["row_data"][routed:] == 0x5A).all() and (gpu["row_scale"][routed:] == 0x5A).all()
+    assert (gpu["col_data"][k * routed // 2:] == 0x5A).all()
+    assert (gpu["col_scale"][k * routed // 16:] == 0x5A).all()
+
+
+def test_graph_replay_changed_routing_equals_host_split():
+    """One capture of the graph-safe amax + four-over-six cast, replayed
+    under three routings: each replay is byte-identical to the host-split
+    calls for that routing, and the first equals the oracle."""
+    k, cap, E = 768, 2048, 4
+    w = synth.random_case(44, [cap], k, "normal")
+    x_dev = to_device(w.x)
+    routings = [[512, 0, 1024, 512], [128, 1664, 128, 128], [0, 0, 0, 1920]]
+    offs = torch.zeros(E, dtype=torch.int32, device="cuda:0")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    bufs = B.alloc_outputs(cap, k, E)
+    offs.copy_(torch.tensor(B.offsets_from_splits(routings[0]), dtype=torch.int32, device="cuda:0"))
+
+    def step():
+        B.nvfp4_group_amax_graphsafe(x_dev, E, offs, status, bufs["row_amax"], bufs["col_amax"])
+        B.nvfp4_group_cast_4over6_graphsafe(x_dev, E, offs, status, **bufs, scale_bound=256, err_mode=B.ERR_MAE)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for n, sp in enumerate(routings):
+        log(f"4over6 graph replay {n} routing {sp}")
+        offs.copy_(torch.tensor(B.offsets_from_splits(sp), dtype=torch.int32, device="cuda:0"))
+        for t in bufs.values():
+            t.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        routed = sum(sp)
+        host = B.alloc_outputs(routed, k, E)
+        B.nvfp4_group_amax(x_dev[:routed], sp, host["row_amax"], host["col_amax"])
+        B.nvfp4_group_cast_4over6(x_dev[:routed], sp, **host, scale_bound=256, err_mode=B.ERR_MAE)
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["row_amax"][:routed], host["row_amax"])
+        assert torch.equal(bufs["col_amax"], host["col_amax"])
+        assert torch.equal(bufs["row_data"][:routed], host["row_data"])
+        assert torch.equal(bufs["row_scale"][:routed], host["row_scale"])
+        assert torch.equal(bufs["col_data"][:k * routed // 2], host["col_data"])
+        assert torch.equal(bufs["col_scale"][:k * routed // 16], host["col_scale"])
+        if n == 0:
+            ref = O.group_quantize_4o6(w.x[:routed], sp, 256, B.ERR_MAE)
+            assert np.array_equal(host["row_data"].cpu().numpy(), ref["row_data"])
+            assert np.array_equal(host["col_data"].cpu().numpy(), ref["col_data"])
+            assert np.array_equal(host["row_scale"].cpu().numpy(), ref["row_scale"])
+            assert np.array_equal(host["col_scale"].cpu().numpy(), ref["col_scale"])
+
+
+FULL = [("deepseek_share", 256, B.ERR_MSE), ("down_proj", 448, B.ERR_MAE)]
+
+
+@pytest.mark.parametrize("name,bound,mode", FULL)
+def test_full_size_every_byte(name, bound, mode):
+    """The expert-share (65536 x 7168, 32 experts) and down-projection
+    (131072 x 2048, 64 experts) workloads, both directions: every amax, data
+    byte and scale byte against the oracle (run as independent row-range and
+    column-range calls on a thread pool)."""
+    w = getattr(synth, name)()
+    splits = list(map(int, w.splits))
+    log(f"4over6 full size {name} bound={bound} mode={mode}: GPU")
+    x_dev = to_device(w.x)
+    bufs = B.alloc_outputs(w.sum_m, w.k, len(splits))
+    B.nvfp4_group_amax(x_dev, splits, bufs["row_amax"], bufs["col_amax"])
+    B.nvfp4_group_cast_4over6(x_dev, splits, **bufs, scale_bound=bound, err_mode=mode)
+    torch.cuda.synchronize()
+    gpu = {key: t.cpu().numpy() for key, t in bufs.items()}
+    del x_dev, bufs
+    log(f"4over6 full size {name}: oracle")
+    ref = OP.group_quantize(w.x, splits, True, True, four_over_six=(bound, mode))
+    log(f"4over6 full size {name}: compare")
+    for key in ("row_amax", "col_amax"):
+        assert np.array_equal(gpu[key].view(np.uint32), ref[key].view(np.uint32)), key
+    for key in ("row_data", "row_scale", "col_data", "col_scale"):
+        a, b = gpu[key].reshape(-1), ref[key].reshape(-1)
+        bad = np.count_nonzero(a != b)
+        assert bad == 0, f"{key}: {bad} mismatching bytes"

@@ -42,6 +42,7 @@ def lib():
     L.selftest_e4m3_exhaustive.argtypes = [P]
     L.selftest_block_step_sample.argtypes = [P, P, ctypes.c_int64, P, P]
     L.selftest_fp4_codes.argtypes = [P, ctypes.c_int64, P]
+    L.selftest_fp4_decode.argtypes = [P]
     return L
 
 
@@ -124,3 +125,20 @@ def test_fp4_codes_match_oracle(lib):
     assert lib.selftest_fp4_codes(ptr(dv), v.size, ptr(codes)) == 0
     torch.cuda.synchronize()
     assert (codes.cpu().numpy() == O.e2m1_encode(v)).all()
+
+
+def test_fp4_decode_equals_e2m1_values(lib):
+    """The four-over-six cast dequantises each candidate's codes with the
+    hardware FP4 -> fp32 convert at unit scale: on every byte, at every byte
+    position of the word, both nibbles decode to the E2M1 value of the
+    oracle (zero codes compare equal whatever the sign of the zero)."""
+    log("fp4 decode, 256 bytes x 4 positions")
+    out = torch.empty(2048, dtype=torch.float32, device="cuda:0")
+    assert lib.selftest_fp4_decode(ptr(out)) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(256, 4, 2)
+    val = np.array([O.e2m1_value(c) for c in range(16)], dtype=np.float32)
+    for byte in range(256):
+        for sel in range(4):
+            assert got[byte, sel, 0] == val[byte & 15], (byte, sel)
+            assert got[byte, sel, 1] == val[byte >> 4], (byte, sel)

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
         "nvfp4_group_dequant_rowwise", "nvfp4_group_dequant_columnwise",
         "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
         "nvfp4_group_gemm", "nvfp4_group_gemm_graphsafe", "nvfp4_group_gemm_wgrad",
-        "nvfp4_group_gemm_wgrad_graphsafe", "nvfp4_group_strerror",
+        "nvfp4_group_gemm_wgrad_graphsafe", "nvfp4_group_cast_4over6", "nvfp4_group_cast_4over6_graphsafe",
+        "nvfp4_group_strerror",
     }
 
 
@@ -54,8 +55,13 @@ def test_binding_constants_match_the_header():
             if hasattr(binding, attr):
                 assert getattr(binding, attr) == value, (name, getattr(binding, attr), value)
                 checked.add(attr)
+    for name, attr in (("NVFP4G_4O6_ERR_MSE", "ERR_MSE"), ("NVFP4G_4O6_ERR_MAE", "ERR_MAE"),
+                       ("NVFP4G_4O6_MAX_BOUND", "MAX_4O6_BOUND"), ("NVFP4G_4O6_DEFAULT_BOUND", "DEFAULT_4O6_BOUND")):
+        value = int(re.search(r"#define %s (\d+)" % name, text).group(1))
+        assert getattr(binding, attr) == value, name
+        checked.add(attr)
     assert {"NVFP4G_OK", "NVFP4G_EHIP", "NVFP4G_DEV_OVERFLOW", "MAX_EXPERTS_HOST", "MAX_EXPERTS_DEVICE",
-            "SMALL_MAX_EXPERT_ELEMS", "SMALL_MAX_K"} <= checked
+            "SMALL_MAX_EXPERT_ELEMS", "SMALL_MAX_K", "ERR_MSE", "MAX_4O6_BOUND"} <= checked
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -204,3 +210,29 @@ def test_gemm_host_checks(lib):
     assert wg(*ok, 256, 32, 32, 2, None, FAKE, FAKE, None) == -1  # no device offsets
     assert wg(*ok, 256, 32, 32, 2, FAKE, FAKE, None, None) == -1  # no status word
     assert wg(*ok, 1 << 23, 32, 32, 2, FAKE, FAKE, FAKE, None) == -1  # capacity above 2^22 rows
+
+
+def test_4over6_host_checks(lib):
+    """The four-over-six knobs are checked on the host: scale bound in
+    1 .. 448, error mode 0 (squared) or 1 (absolute); the rest as in the cast."""
+    f = lib.nvfp4_group_cast_4over6
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 5
+    sp = (ctypes.c_int64 * 1)(128)
+    out = [FAKE, FAKE, None, None]
+    assert f(FAKE, 128, 32, 1, sp, FAKE, None, 0, 0, *out, None) == -1      # bound 0
+    assert f(FAKE, 128, 32, 1, sp, FAKE, None, 449, 0, *out, None) == -1    # bound above 448
+    assert f(FAKE, 128, 32, 1, sp, FAKE, None, 256, 2, *out, None) == -1    # unknown error mode
+    assert f(FAKE, 128, 32, 1, sp, FAKE, None, 256, -1, *out, None) == -1
+    assert f(FAKE, 128, 32, 1, sp, None, None, 256, 0, *out, None) == -1    # rowwise data without row amax
+    assert f(FAKE, 128, 32, 1, sp, FAKE, None, 256, 0, FAKE + 4, FAKE, None, None, None) == -3  # misaligned
+    bad = (ctypes.c_int64 * 1)(100)
+    assert f(FAKE, 100, 32, 1, bad, FAKE, None, 256, 0, *out, None) == -2   # split not a multiple of 128
+    g = lib.nvfp4_group_cast_4over6_graphsafe
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 6
+    assert g(FAKE, 256, 32, 2, None, FAKE, None, 256, 0, *out, FAKE, None) == -1   # no device offsets
+    assert g(FAKE, 256, 32, 2, FAKE, FAKE, None, 256, 0, *out, None, None) == -1   # no status word
+    assert g(FAKE, 256, 32, 2, FAKE, FAKE, None, 1000, 0, *out, FAKE, None) == -1  # bound out of range
