@@ -305,6 +305,8 @@ def main():
     ap.add_argument("--graph-replays", type=int, default=100)
     ap.add_argument("--next-rows", type=int, default=20,
                     help="launches timed for each of the MXFP4 cast and the two dequants (0: skip)")
+    ap.add_argument("--next-only", default=None, choices=("mxfp4", "dequant", "four_over_six", "gemm"),
+                    help="run only this group of next rows (for profiling one kernel)")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="also time the steps with a read of this many MB before each (outside the timed "
                          "events), so that no input or output is left in the 256 MB memory-side cache (0: skip)")
@@ -393,7 +395,7 @@ def main():
         del src, dst
 
     if w.rowwise and w.columnwise and args.next_rows > 0:
-        result["next_rows"] = next_rows(B, torch, tev, x, splits, out, E, k, m, args.next_rows)
+        result["next_rows"] = next_rows(B, torch, tev, x, splits, out, E, k, m, args.next_rows, args.next_only)
     del x, out
     torch.cuda.empty_cache()
 
@@ -498,7 +500,7 @@ def hbm_ceiling(torch, tev, dev, w, x, out, reps: int = 10) -> dict:
     return res
 
 
-def next_rows(B, torch, tev, x, splits, out, E: int, k: int, m: int, reps: int) -> dict:
+def next_rows(B, torch, tev, x, splits, out, E: int, k: int, m: int, reps: int, only=None) -> dict:
     """MXFP4 cast of the step's input and NVFP4 dequant of its outputs."""
     print("[bench] MXFP4 cast and dequant", file=sys.stderr, flush=True)
     N = m * k
@@ -520,20 +522,24 @@ def next_rows(B, torch, tev, x, splits, out, E: int, k: int, m: int, reps: int) 
                 "GBps": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
     res = {}
-    mx = B.alloc_mx_outputs(m, k, device=x.device)
-    ms = timed(lambda: B.mxfp4_group_cast(x, splits, **mx))
-    res["mxfp4_group_cast"] = entry("mxfp4_group_cast_kernel", ms, 2 * N + 2 * (N // 2 + N // 32))
-    del mx
-    deq = torch.empty(N, dtype=torch.float32, device=x.device)
-    ms = timed(lambda: B.nvfp4_group_dequant_rowwise(out["row_data"], out["row_scale"], out["row_amax"],
-                                                      deq.view(m, k)))
-    res["nvfp4_group_dequant_rowwise"] = entry("dequant_kernel", ms, N // 2 + N // 16 + 4 * m + 4 * N)
-    ms = timed(lambda: B.nvfp4_group_dequant_columnwise(out["col_data"], out["col_scale"], out["col_amax"],
-                                                         splits, k, deq))
-    res["nvfp4_group_dequant_columnwise"] = entry("dequant_kernel", ms, N // 2 + N // 16 + 4 * E * k + 4 * N)
-    del deq
-    res.update(four_over_six_rows(B, torch, timed, entry, x, splits, out, E, k, m))
-    res.update(gemm_rows(B, torch, timed, out, splits, E, k, m))
+    if only in (None, "mxfp4"):
+        mx = B.alloc_mx_outputs(m, k, device=x.device)
+        ms = timed(lambda: B.mxfp4_group_cast(x, splits, **mx))
+        res["mxfp4_group_cast"] = entry("mxfp4_group_cast_kernel", ms, 2 * N + 2 * (N // 2 + N // 32))
+        del mx
+    if only in (None, "dequant"):
+        deq = torch.empty(N, dtype=torch.float32, device=x.device)
+        ms = timed(lambda: B.nvfp4_group_dequant_rowwise(out["row_data"], out["row_scale"], out["row_amax"],
+                                                          deq.view(m, k)))
+        res["nvfp4_group_dequant_rowwise"] = entry("dequant_kernel", ms, N // 2 + N // 16 + 4 * m + 4 * N)
+        ms = timed(lambda: B.nvfp4_group_dequant_columnwise(out["col_data"], out["col_scale"], out["col_amax"],
+                                                             splits, k, deq))
+        res["nvfp4_group_dequant_columnwise"] = entry("dequant_kernel", ms, N // 2 + N // 16 + 4 * E * k + 4 * N)
+        del deq
+    if only in (None, "four_over_six"):
+        res.update(four_over_six_rows(B, torch, timed, entry, x, splits, out, E, k, m))
+    if only in (None, "gemm"):
+        res.update(gemm_rows(B, torch, timed, out, splits, E, k, m))
     return res
 
 

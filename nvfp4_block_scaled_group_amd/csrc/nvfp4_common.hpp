@@ -99,6 +99,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // Cache policy bits: streaming (non-temporal) loads of x; plain stores.
 constexpr int kLoadStream = 2;
+// Load policy of the amax pass and of the cast's tile loads (both streaming
+// by default; overridable at build time for measurements).
+#ifndef NVFP4G_AMAX_LOAD_AUX
+#define NVFP4G_AMAX_LOAD_AUX 2
+#endif
+#ifndef NVFP4G_CAST_LOAD_AUX
+#define NVFP4G_CAST_LOAD_AUX 2
+#endif
+constexpr int kAmaxLoadAux = NVFP4G_AMAX_LOAD_AUX;
+constexpr int kCastLoadAux = NVFP4G_CAST_LOAD_AUX;
 #ifndef NVFP4G_STORE_AUX
 #define NVFP4G_STORE_AUX 0
 #endif
@@ -145,7 +155,7 @@ __device__ __forceinline__ void load_tile(const uint16_t* tile, uint32_t ku, uin
   const rsrc_t xr = make_rsrc(tile);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, vo, (uint32_t)i * ku * 2u, kLoadStream);
+    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, vo, (uint32_t)i * ku * 2u, kCastLoadAux);
     v[i][0] = q.x; v[i][1] = q.y; v[i][2] = q.z; v[i][3] = q.w;
   }
 }

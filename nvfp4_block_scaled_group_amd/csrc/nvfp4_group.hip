@@ -88,7 +88,7 @@ __device__ __forceinline__ void amax_load(const uint16_t* x, uint32_t ku, int32_
   const rsrc_t xr = make_rsrc(x + (int64_t)row0 * ku + (int64_t)chunk * kAmaxCols);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, lane_off, (uint32_t)i * ku * 2u, kLoadStream);
+    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, lane_off, (uint32_t)i * ku * 2u, kAmaxLoadAux);
     v[i][0] = q.x; v[i][1] = q.y; v[i][2] = q.z; v[i][3] = q.w;
   }
 }
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void group_amax_rows_kernel(
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, off[c], (uint32_t)r * ku * 2u, kLoadStream);
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(xr, off[c], (uint32_t)r * ku * 2u, kAmaxLoadAux);
         v[r][c][0] = q.x; v[r][c][1] = q.y; v[r][c][2] = q.z; v[r][c][3] = q.w;
       }
   };
