@@ -25,11 +25,9 @@
 //    sums run in the lane in row order.
 //  * Rowwise blocks are split over the lane pair (L, L^8) (8 columns each).
 //    The even lane owns row i of the pair of rows (i, 8+i) it serves with
-//    its partner and the odd lane row 8+i; each lane computes the error terms
-//    of its 8 columns of both rows, then two masked DPP moves per term give
-//    each lane all 16 terms of its own row in element order (the even lane
-//    takes its partner's second half, the odd lane its partner's first
-//    half), and the lane sums them in order.
+//    its partner and the odd lane row 8+i; two masked DPP moves per data
+//    word give each lane the 16 values of its own row's block in element
+//    order, and it then encodes the block alone, like a columnwise one.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <float.h>
@@ -73,16 +71,6 @@ __device__ __forceinline__ float err_term(float x, float q, float sv, float s) {
   return MODE == 0 ? diff * diff : fabsf(diff);
 }
 
-// Codes of 8 values (v = 4 words of bf16 pairs) times m, 2 per byte.
-__device__ __forceinline__ uint32_t encode8(const uint32_t (&v)[4], float m) {
-  uint32_t p = 0;
-  p = FP4X2(p, bf16lo(v[0]) * m, bf16hi(v[0]) * m, 0);
-  p = FP4X2(p, bf16lo(v[1]) * m, bf16hi(v[1]) * m, 1);
-  p = FP4X2(p, bf16lo(v[2]) * m, bf16hi(v[2]) * m, 2);
-  p = FP4X2(p, bf16lo(v[3]) * m, bf16hi(v[3]) * m, 3);
-  return p;
-}
-
 // The 8 values of a packed code word, in element order.
 __device__ __forceinline__ void decode8(uint32_t p, float (&q)[8]) {
   const auto q0 = FP4X2_VALUE(p, 0), q1 = FP4X2_VALUE(p, 1), q2 = FP4X2_VALUE(p, 2), q3 = FP4X2_VALUE(p, 3);
@@ -100,37 +88,45 @@ __device__ __forceinline__ uint32_t encode8f(const float* x, float m) {
   return p;
 }
 
-// The 8 error terms of the values v (codes p) for one candidate.
+// Error sum of one candidate over a block of 16 values x (element order),
+// codes c_lo (elements 0-7) and c_hi (8-15), scale value sv, line scale s:
+// ((0 + r_0) + r_1) + ... + r_15.
 template <int MODE>
-__device__ __forceinline__ void terms8(const uint32_t (&v)[4], uint32_t p, float sv, float s, float (&t)[8]) {
-  float q[8];
-  decode8(p, q);
+__device__ __forceinline__ float block_err(const float (&x)[16], uint32_t c_lo, uint32_t c_hi, float sv, float s) {
+  float q[16];
+  decode8(c_lo, *reinterpret_cast<float(*)[8]>(&q[0]));
+  decode8(c_hi, *reinterpret_cast<float(*)[8]>(&q[8]));
+  float e = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    t[2 * j] = err_term<MODE>(bf16lo(v[j]), q[2 * j], sv, s);
-    t[2 * j + 1] = err_term<MODE>(bf16hi(v[j]), q[2 * j + 1], sv, s);
-  }
+  for (int i = 0; i < 16; ++i) e = e + err_term<MODE>(x[i], q[i], sv, s);
+  return e;
+}
+
+// Four-over-six step of one block of 16 values x (element order) with block
+// amax b on a line with scale s: both candidates, the one with the smaller
+// error kept (6 on a tie).  Returns its scale code; *lo, *hi = its codes of
+// elements 0-7 and 8-15 (element 2j in the low nibble of byte j).
+template <int MODE>
+__device__ __forceinline__ uint32_t block_4o6(const float (&x)[16], float b, float s, uint32_t* lo, uint32_t* hi) {
+  float sv6, m6, sv4, m4;
+  const uint32_t S6 = cand_step(b, kK6, s, &sv6, &m6);
+  const uint32_t S4 = cand_step(b, kK4, s, &sv4, &m4);
+  const uint32_t c6_lo = encode8f(x, m6), c6_hi = encode8f(x + 8, m6);
+  const uint32_t c4_lo = encode8f(x, m4), c4_hi = encode8f(x + 8, m4);
+  const float e6 = block_err<MODE>(x, c6_lo, c6_hi, sv6, s);
+  const float e4 = block_err<MODE>(x, c4_lo, c4_hi, sv4, s);
+  const bool use4 = e4 < e6;
+  *lo = use4 ? c4_lo : c6_lo;
+  *hi = use4 ? c4_hi : c6_hi;
+  return use4 ? S4 : S6;
 }
 
 // DPP row_ror:8 (lane ^ 8 inside a 16-lane row) written only to the lanes
 // 0-7 (BANKS = 0x3) or 8-15 (BANKS = 0xC) of each row; the other lanes keep
 // `old`.
 template <int BANKS>
-__device__ __forceinline__ float swap8_into(float old, float src) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), 0x128, 0xF, BANKS, false));
-}
-
-// Error sum, in element order, of the rowwise block this lane owns: a = the
-// lane's terms of row i (elements 0-7 in the even lane, 8-15 in the odd
-// lane), c = those of row 8+i.  The even lane owns row i: its own a, then the
-// partner's a.  The odd lane owns row 8+i: the partner's c, then its own c.
-__device__ __forceinline__ float row_block_sum(const float (&a)[8], const float (&c)[8]) {
-  float e = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) e = e + swap8_into<0xC>(a[j], c[j]);  // first half
-#pragma unroll
-  for (int j = 0; j < 8; ++j) e = e + swap8_into<0x3>(c[j], a[j]);  // second half
-  return e;
+__device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x128, 0xF, BANKS, false);
 }
 
 template <int MODE>
@@ -172,96 +168,56 @@ __global__ __launch_bounds__(kThreads) void group_cast_4o6_kernel(
   __syncthreads();
 
   if (row_data) {
+    // The lane pair (lane, lane^8) holds the two 8-column halves of each
+    // 16-column block of its 16 rows.  Iteration i serves rows i and 8+i:
+    // the even lane takes row i's block (its own half, then the partner's),
+    // the odd lane row 8+i's (the partner's half, then its own), by two
+    // masked DPP moves per word, and each lane encodes its block alone.
     const bool odd = cg & 1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // block amax of the owned row (as in the grouped cast)
-      const uint32_t lo = hmax(pkmax(pkmax(v[i][0] & 0x7FFF7FFFu, v[i][1] & 0x7FFF7FFFu),
-                                     pkmax(v[i][2] & 0x7FFF7FFFu, v[i][3] & 0x7FFF7FFFu)));
-      const uint32_t hi = hmax(pkmax(pkmax(v[8 + i][0] & 0x7FFF7FFFu, v[8 + i][1] & 0x7FFF7FFFu),
-                                     pkmax(v[8 + i][2] & 0x7FFF7FFFu, v[8 + i][3] & 0x7FFF7FFFu)));
-      const uint32_t b16 = max(odd ? hi : lo, swap8(odd ? lo : hi));
-      const float b = __uint_as_float(b16 << 16);
-      const float s_lo = l_row[16 * rb + i], s_hi = l_row[16 * rb + 8 + i];
-      const float s_own = odd ? s_hi : s_lo;
-      float sv6, m6, sv4, m4;
-      const uint32_t S6 = cand_step(b, kK6, s_own, &sv6, &m6);
-      const uint32_t S4 = cand_step(b, kK4, s_own, &sv4, &m4);
-      // the partner's candidates serve this lane's half of the other row
-      const float psv6 = __uint_as_float(swap8(__float_as_uint(sv6)));
-      const float pm6 = __uint_as_float(swap8(__float_as_uint(m6)));
-      const float psv4 = __uint_as_float(swap8(__float_as_uint(sv4)));
-      const float pm4 = __uint_as_float(swap8(__float_as_uint(m4)));
-      const float m6_lo = odd ? pm6 : m6, m6_hi = odd ? m6 : pm6;
-      const float m4_lo = odd ? pm4 : m4, m4_hi = odd ? m4 : pm4;
-      const float sv6_lo = odd ? psv6 : sv6, sv6_hi = odd ? sv6 : psv6;
-      const float sv4_lo = odd ? psv4 : sv4, sv4_hi = odd ? sv4 : psv4;
-
-      const uint32_t p6_lo = encode8(v[i], m6_lo), p6_hi = encode8(v[8 + i], m6_hi);
-      const uint32_t p4_lo = encode8(v[i], m4_lo), p4_hi = encode8(v[8 + i], m4_hi);
-      float e6, e4;
-      {
-        float a[8], c[8];
-        terms8<MODE>(v[i], p6_lo, sv6_lo, s_lo, a);
-        terms8<MODE>(v[8 + i], p6_hi, sv6_hi, s_hi, c);
-        e6 = row_block_sum(a, c);
+      uint32_t w[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[q] = swap8_into<0xC>(v[i][q], v[8 + i][q]);      // elements 0-7
+        w[4 + q] = swap8_into<0x3>(v[8 + i][q], v[i][q]);  // elements 8-15
       }
-      {
-        float a[8], c[8];
-        terms8<MODE>(v[i], p4_lo, sv4_lo, s_lo, a);
-        terms8<MODE>(v[8 + i], p4_hi, sv4_hi, s_hi, c);
-        e4 = row_block_sum(a, c);
+      uint32_t mx = 0;
+      float xv[16];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        mx = pkmax(mx, w[q] & 0x7FFF7FFFu);
+        xv[2 * q] = bf16lo(w[q]);
+        xv[2 * q + 1] = bf16hi(w[q]);
       }
-      const uint32_t use4 = e4 < e6 ? 1u : 0u;  // this lane's row
-      const uint32_t puse4 = swap8(use4);       // the partner's row
-      const bool use4_lo = odd ? puse4 : use4, use4_hi = odd ? use4 : puse4;
       const int ri = odd ? 8 + i : i;
-      reinterpret_cast<uint8_t*>(&l_rs[16 * rb + ri][0])[wave * 4 + (cg >> 1)] = (uint8_t)(use4 ? S4 : S6);
-      l_rd[16 * rb + i][row_slot(rb, wave, cg)] = use4_lo ? p4_lo : p6_lo;
-      l_rd[16 * rb + 8 + i][row_slot(rb, wave, cg)] = use4_hi ? p4_hi : p6_hi;
+      uint32_t lo, hi;
+      const uint32_t S = block_4o6<MODE>(xv, __uint_as_float(hmax(mx) << 16), l_row[16 * rb + ri], &lo, &hi);
+      reinterpret_cast<uint8_t*>(&l_rs[16 * rb + ri][0])[wave * 4 + (cg >> 1)] = (uint8_t)S;
+      // bytes of columns 8*(cg & ~1) .. +15: dwords 8*wave + (cg & ~1), +1 of the row
+      *reinterpret_cast<u32x2*>(&l_rd[16 * rb + ri][row_slot(rb, wave, cg & ~1)]) = u32x2{lo, hi};
     }
   }
 
   if (col_data) {
     const rsrc_t cd = make_rsrc(col_data + k * (int64_t)rbeg / 2 + col_base * (me / 2) + (row0 - rbeg) / 2);
     const uint32_t vo = active ? lcol * (me / 2) + 8u * rb : kOutOfRange;
+    uint32_t mxw[4] = {0, 0, 0, 0};  // column maxima, two columns per word
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mxw[q] = pkmax(mxw[q], v[i][q] & 0x7FFF7FFFu);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // column lcol + j of the lane's 16 rows
       float xv[16];
-      uint32_t mx = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t w = (j & 1) ? (v[i][j >> 1] >> 16) : (v[i][j >> 1] & 0xFFFFu);
-        xv[i] = __uint_as_float(w << 16);
-        mx = max(mx, w & 0x7FFFu);
-      }
-      const float b = __uint_as_float(mx << 16);
-      const float s = l_col[lcol + j];
-      float sv6, m6, sv4, m4;
-      const uint32_t S6 = cand_step(b, kK6, s, &sv6, &m6);
-      const uint32_t S4 = cand_step(b, kK4, s, &sv4, &m4);
-      const uint32_t c6_lo = encode8f(xv, m6), c6_hi = encode8f(xv + 8, m6);
-      const uint32_t c4_lo = encode8f(xv, m4), c4_hi = encode8f(xv + 8, m4);
-      float e6 = 0.0f, e4 = 0.0f;
-      {
-        float q[16];
-        decode8(c6_lo, *reinterpret_cast<float(*)[8]>(&q[0]));
-        decode8(c6_hi, *reinterpret_cast<float(*)[8]>(&q[8]));
-#pragma unroll
-        for (int i = 0; i < 16; ++i) e6 = e6 + err_term<MODE>(xv[i], q[i], sv6, s);
-      }
-      {
-        float q[16];
-        decode8(c4_lo, *reinterpret_cast<float(*)[8]>(&q[0]));
-        decode8(c4_hi, *reinterpret_cast<float(*)[8]>(&q[8]));
-#pragma unroll
-        for (int i = 0; i < 16; ++i) e4 = e4 + err_term<MODE>(xv[i], q[i], sv4, s);
-      }
-      const bool use4 = e4 < e6;
-      reinterpret_cast<uint8_t*>(&l_cs[lcol + j][0])[rb] = (uint8_t)(use4 ? S4 : S6);
-      __builtin_amdgcn_raw_buffer_store_b64(use4 ? u32x2{c4_lo, c4_hi} : u32x2{c6_lo, c6_hi}, cd, vo,
-                                            (uint32_t)j * (me / 2), kStoreStream);
+      for (int i = 0; i < 16; ++i) xv[i] = (j & 1) ? bf16hi(v[i][j >> 1]) : bf16lo(v[i][j >> 1]);
+      const uint32_t b16 = (j & 1) ? (mxw[j >> 1] >> 16) : (mxw[j >> 1] & 0xFFFFu);
+      uint32_t lo, hi;
+      const uint32_t S = block_4o6<MODE>(xv, __uint_as_float(b16 << 16), l_col[lcol + j], &lo, &hi);
+      reinterpret_cast<uint8_t*>(&l_cs[lcol + j][0])[rb] = (uint8_t)S;
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, cd, vo, (uint32_t)j * (me / 2), kStoreStream);
     }
   }
 
