@@ -2,7 +2,8 @@
 CPU oracle's four-over-six cast, element by element and bit-exact: small and
 ragged shapes for every error mode and several scale bounds, each direction
 alone, the graph-safe form under partial routing and under graph replay with
-changed routing, and the two full-size expert workloads on every byte.
+changed routing, the two full-size expert workloads on every byte, empty
+inputs, and the ABI's size limits (2^24 rows, K = 2^22) on sampled lines.
 
 The amax comes from the library's grouped amax (checked equal to the
 oracle's); the four-over-six cast consumes it."""
@@ -203,3 +204,109 @@ def test_full_size_every_byte(name, bound, mode):
         a, b = gpu[key].reshape(-1), ref[key].reshape(-1)
         bad = np.count_nonzero(a != b)
         assert bad == 0, f"{key}: {bad} mismatching bytes"
+
+
+def test_empty_inputs():
+    """No routed rows: the host-split call with all-empty experts and the
+    graph-safe call with zero offsets succeed and write nothing."""
+    k = 64
+    x = torch.zeros((0, k), dtype=torch.int16, device="cuda:0")
+    out = B.alloc_outputs(0, k, 3)
+    log("4over6 empty host-split call")
+    B.nvfp4_group_amax(x, [0, 0, 0], out["row_amax"], out["col_amax"])
+    B.nvfp4_group_cast_4over6(x, [0, 0, 0], **out)
+    cap = 256
+    xc = torch.zeros((cap, k), dtype=torch.int16, device="cuda:0")
+    o = alloc(cap, k, 3, True, True)
+    for g in o.values():
+        g.t.view(torch.uint8).fill_(0x5A)
+    t = tensors(o)
+    t["row_amax"].zero_()
+    t["col_amax"].zero_()
+    offs = torch.zeros(3, dtype=torch.int32, device="cuda:0")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    log("4over6 empty graph-safe call")
+    B.nvfp4_group_cast_4over6_graphsafe(xc, 3, offs, status, **t)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert_guards(o)
+    for key in ("row_data", "row_scale", "col_data", "col_scale"):
+        assert (o[key].numpy() == 0x5A).all(), key
+
+
+def _line_ref(L, A, bound, mode):
+    d, s, _ = O.encode_line_4o6(synth.bf16_bits_to_f32(L), float(A), bound, mode)
+    return d, s
+
+
+def test_row_limit_2_to_24_rows():
+    """2^24 rows at K = 16 (two experts, one of 2^24 - 2^17 rows): the
+    largest row offsets.  Sampled rows (both ends of each expert and random
+    ones) and whole column lines against the oracle's line encoder."""
+    bound, mode = 256, B.ERR_MSE
+    log("4over6 row limit: generating 2^24 x 16")
+    w = synth.max_rows()
+    splits = list(map(int, w.splits))
+    x = to_device(w.x)
+    out = B.alloc_outputs(w.sum_m, w.k, len(splits))
+    B.nvfp4_group_amax(x, splits, out["row_amax"], out["col_amax"])
+    B.nvfp4_group_cast_4over6(x, splits, **out, scale_bound=bound, err_mode=mode)
+    torch.cuda.synchronize()
+    res = {key: t.cpu().numpy() for key, t in out.items()}
+    del x, out
+    rng = np.random.default_rng(61)
+    offs = np.concatenate([[0], np.cumsum(splits)]).astype(np.int64)
+    rows = set(rng.integers(0, w.sum_m, 2000).tolist())
+    for e in range(len(splits)):
+        rows |= {int(offs[e]), int(offs[e]) + 1, int(offs[e + 1]) - 1}
+    log(f"4over6 row limit: {len(rows)} rows vs oracle")
+    for r in sorted(rows):
+        d, s = _line_ref(w.x[r], res["row_amax"][r], bound, mode)
+        assert np.array_equal(res["row_data"][r], d) and np.array_equal(res["row_scale"][r], s), f"row {r}"
+    k = w.k
+    for e in range(len(splits)):
+        r0, m = int(offs[e]), splits[e]
+        for c in (0, 7, 15):
+            log(f"4over6 row limit: expert {e} column {c} ({m} rows) vs oracle")
+            d, s = _line_ref(np.ascontiguousarray(w.x[r0:r0 + m, c]), res["col_amax"][e * k + c], bound, mode)
+            d0, s0 = k * r0 // 2 + c * (m // 2), k * r0 // 16 + c * (m // 16)
+            assert np.array_equal(res["col_data"][d0:d0 + m // 2], d), f"col_data expert {e} column {c}"
+            assert np.array_equal(res["col_scale"][s0:s0 + m // 16], s), f"col_scale expert {e} column {c}"
+
+
+def test_column_limit_k_2_to_22():
+    """K = 2^22 (one expert of 128 rows): the largest column offsets.
+    Sampled rows and 20000 sampled column lines against the oracle's line
+    encoder, and the graph-safe call byte-identical to the host-split one."""
+    bound, mode = 448, B.ERR_MAE
+    log("4over6 column limit: generating 128 x 2^22")
+    w = synth.max_k()
+    splits = list(map(int, w.splits))
+    x = to_device(w.x)
+    out = B.alloc_outputs(w.sum_m, w.k, 1)
+    B.nvfp4_group_amax(x, splits, out["row_amax"], out["col_amax"])
+    B.nvfp4_group_cast_4over6(x, splits, **out, scale_bound=bound, err_mode=mode)
+    g = B.alloc_outputs(w.sum_m, w.k, 1)
+    g["row_amax"].copy_(out["row_amax"])
+    g["col_amax"].copy_(out["col_amax"])
+    offs = torch.tensor([w.sum_m], dtype=torch.int32, device="cuda:0")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    B.nvfp4_group_cast_4over6_graphsafe(x, 1, offs, status, **g, scale_bound=bound, err_mode=mode)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for key in out:
+        assert torch.equal(out[key], g[key]), key
+    res = {key: t.cpu().numpy() for key, t in out.items()}
+    del x, out, g
+    k, m = w.k, w.sum_m
+    for r in (0, 1, 63, 126, 127):
+        log(f"4over6 column limit: row {r} vs oracle")
+        d, s = _line_ref(w.x[r], res["row_amax"][r], bound, mode)
+        assert np.array_equal(res["row_data"][r], d) and np.array_equal(res["row_scale"][r], s), f"row {r}"
+    rng = np.random.default_rng(62)
+    cols = np.unique(np.concatenate([rng.integers(0, k, 20000), [0, 1, k - 2, k - 1]]))
+    log(f"4over6 column limit: {cols.size} column lines vs oracle")
+    for c in cols.tolist():
+        d, s = _line_ref(np.ascontiguousarray(w.x[:, c]), res["col_amax"][c], bound, mode)
+        assert np.array_equal(res["col_data"][c * (m // 2):(c + 1) * (m // 2)], d), f"col_data column {c}"
+        assert np.array_equal(res["col_scale"][c * (m // 16):(c + 1) * (m // 16)], s), f"col_scale column {c}"
