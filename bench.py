@@ -38,7 +38,9 @@ Beside the headline the line carries:
   GEMM (forward and weight gradient, MFMA-bound, TFLOP/s against the fp16
   MFMA peak) with torch.matmul (hipBLASLt) fp16 on the same shapes beside it;
 - ``cpu_baseline``: the CPU oracle over the whole workload on the host's
-  threads (at most 16), timed before the process touches the GPU.
+  threads (at most 16), timed before the process touches the GPU; each
+  entry of ``configs`` carries the same figure for its own workload
+  (median of 5 runs for the two small ones).
 """
 from __future__ import annotations
 
@@ -149,20 +151,28 @@ def host_cpu() -> dict:
     return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": affinity}
 
 
-def cpu_baseline(w, one_thread_rows: int = 16384, threads: int | None = None) -> dict:
+def cpu_baseline(w, one_thread_rows: int = 16384, threads: int | None = None, reps: int = 1) -> dict:
     """The oracle, as it stands, on the whole workload: independent oracle
     calls (the rowwise direction on row ranges, the columnwise direction on
     column ranges of each expert; together exactly the bytes of one call) on
     a pool of host threads, at most one per CPU of the process's share and at
     most 16 (a one-GPU share of the GPU host).  Also one call on one thread
     over the first whole experts (in expert order) that fit in
-    ``one_thread_rows`` rows.  Runs before the process touches the GPU."""
+    ``one_thread_rows`` rows.  Each timing is the median of ``reps`` runs.
+    Runs before the process touches the GPU."""
     from oracle import oracle as O
     from oracle import parallel as OP
     n = threads or OP.default_threads()
-    t0 = time.perf_counter()
-    OP.group_quantize(w.x, w.splits, w.rowwise, w.columnwise, threads=n)
-    dtn = time.perf_counter() - t0
+
+    def med(fn):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    dtn = med(lambda: OP.group_quantize(w.x, w.splits, w.rowwise, w.columnwise, threads=n))
     b_all = algorithmic_bytes(w.sum_m, w.k, w.num_experts, w.rowwise, w.columnwise)["step"]
     offs = np.concatenate([[0], np.cumsum(w.splits)])
     chosen, rows = [], 0
@@ -172,24 +182,25 @@ def cpu_baseline(w, one_thread_rows: int = 16384, threads: int | None = None) ->
             rows += int(m)
     xs = np.concatenate([w.x[offs[e]:offs[e + 1]] for e in chosen])
     sp = [int(w.splits[e]) for e in chosen]
-    t0 = time.perf_counter()
-    O.group_quantize(xs, sp, w.rowwise, w.columnwise)
-    dt1 = time.perf_counter() - t0
+    dt1 = med(lambda: O.group_quantize(xs, sp, w.rowwise, w.columnwise))
     b1 = algorithmic_bytes(rows, w.k, len(sp), w.rowwise, w.columnwise)["step"]
     ntasks = len(OP.tasks(w.splits, w.k, w.rowwise, w.columnwise))
     res = {"value": round(b_all / dtn / 1e9, 5), "unit": "GB/s", "cores": n, "kind": "oracle",
-           "sample": f"the whole workload ({w.sum_m} rows x K={w.k}, both directions): {ntasks} row-range / "
-                     f"column-range calls of the C oracle on {n} threads, {dtn:.2f} s",
+           "sample": f"the whole workload ({w.sum_m} rows x K={w.k}, {directions(w)}): {ntasks} row-range / "
+                     f"column-range calls of the C oracle on {n} threads, {dtn:.3f} s"
+                     + (f" (median of {reps} runs)" if reps > 1 else ""),
            "seconds": round(dtn, 3), "threads": n,
            "value_one_thread": round(b1 / dt1 / 1e9, 5),
-           "one_thread_sample": f"one call on one thread: {len(sp)} whole experts, {rows} rows, {dt1:.2f} s"}
+           "one_thread_sample": f"one call on one thread: {len(sp)} whole experts, {rows} rows, {dt1:.3f} s"}
     res.update(host_cpu())
     return res
 
 
 WORKLOADS = ["deepseek_share", "down_proj", "outliers", "tiny"]
-# the other configurations reported beside the headline, with their timed steps
+# the other configurations reported beside the headline, with their timed
+# steps and the runs of the CPU oracle timed for each (median)
 SIDE_CONFIGS = {"tiny": 1000, "outliers": 1000, "down_proj": 200}
+SIDE_CPU_REPS = {"tiny": 5, "outliers": 5, "down_proj": 1}
 
 
 def measure_step(B, torch, tev, w, x, out, steps: int, warmup: int, settle_ms: float) -> dict:
@@ -271,12 +282,12 @@ def roofline(profiling, workload: str, kernel: str, nbytes: int, ms: float) -> d
             "algorithmic_bytes_per_launch": nbytes}
 
 
-def side_config(B, synth, torch, tev, profiling, dev, name: str, steps: int) -> dict:
+def side_config(B, torch, tev, profiling, dev, w, name: str, steps: int, cpu=None) -> dict:
     """One of the other configurations: the same step protocol (shorter), its
-    rate against the HBM peak, the kernels' event times, and (where a profile
-    exists) the dominant kernel's measured traffic."""
+    rate against the HBM peak, the kernels' event times, (where a profile
+    exists) the dominant kernel's measured traffic, and the CPU oracle's rate
+    on the same workload (timed before any GPU use)."""
     print(f"[bench] config {name}", file=sys.stderr, flush=True)
-    w = synth.CONFIGS[name]()
     x = torch.from_numpy(w.x.view(np.int16)).to(dev)
     out = B.alloc_outputs(w.sum_m, w.k, w.num_experts, w.rowwise, w.columnwise, device=dev)
     r = measure_step(B, torch, tev, w, x, out, steps, max(20, steps // 10), 30.0)
@@ -286,6 +297,8 @@ def side_config(B, synth, torch, tev, profiling, dev, name: str, steps: int) -> 
            "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": r["nbytes"]["step"],
            "gpu_ms_per_step": round(r["first_ms"] + r["second_ms"], 5), "kernels": r["kernels"],
            "roofline": roofline(profiling, name, r["dom_name"], r["dom_bytes"], r["dom_ms"])}
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     del x, out
     torch.cuda.empty_cache()
     return res
@@ -325,9 +338,13 @@ def main():
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     w = synth.CONFIGS[args.workload]()
     cpu = None
+    side = {} if args.no_configs else {name: synth.CONFIGS[name]() for name in SIDE_CONFIGS if name != args.workload}
+    side_cpu = {}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (before any GPU use)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w)
+        for name, sw in side.items():
+            side_cpu[name] = cpu_baseline(sw, reps=SIDE_CPU_REPS[name])
 
     import torch
     from nvfp4_block_scaled_group_amd import binding as B
@@ -373,10 +390,12 @@ def main():
             flush.max()
             step(fev[i])
         torch.cuda.synchronize()
-        f_ms = float(np.mean([tev.elapsed_ms(e[0], e[2]) for e in fev]))
+        f_all = [tev.elapsed_ms(e[0], e[2]) for e in fev]
+        f_ms = float(np.mean(f_all))
         f1 = float(np.mean([tev.elapsed_ms(e[0], e[1]) for e in fev]))
         result["flushed_step"] = {"flush_mb": args.flush_mb, "steps": args.steps,
-                                  "ms_per_step": round(f_ms, 4),
+                                  "ms_per_step": round(f_ms, 4), "median_ms": round(float(np.median(f_all)), 4),
+                                  "min_ms": round(float(np.min(f_all)), 4),
                                   "GBps": round(nbytes["step"] / (f_ms * 1e-3) / 1e9, 2),
                                   "first_launch_us": round(f1 * 1e3, 2),
                                   "second_launch_us": round((f_ms - f1) * 1e3, 2),
@@ -401,9 +420,9 @@ def main():
 
     if not args.no_configs:
         configs = {}
-        for name, n in SIDE_CONFIGS.items():
-            if name != args.workload:
-                configs[name] = side_config(B, synth, torch, tev, profiling, dev, name, n)
+        for name, sw in side.items():
+            configs[name] = side_config(B, torch, tev, profiling, dev, sw, name, SIDE_CONFIGS[name],
+                                        side_cpu.get(name))
         if args.graph_replays > 0:
             configs["graph_replay"] = graph_replay(B, synth, torch, tev, dev, args.graph_replays)
         result["configs"] = configs
