@@ -50,14 +50,19 @@ def x():
     ("col_scale", torch.zeros(M * K // 8, dtype=torch.uint8)[::2]),  # not contiguous
     ("col_scale", torch.zeros(M * K // 16, dtype=torch.uint8, device="meta")),
 ])
-@pytest.mark.parametrize("entry", ["cast", "quantize", "quantize_graphsafe"])
+@pytest.mark.parametrize("entry", ["cast", "quantize", "quantize_graphsafe", "cast_4over6", "cast_4over6_graphsafe"])
 def test_bad_output_buffer_is_rejected(key, bad, entry):
     out = outputs(**{key: bad})
+    offs, status = torch.tensor([128, 256], dtype=torch.int32), torch.zeros(1, dtype=torch.int32)
     with pytest.raises(ValueError, match=key):
         if entry == "cast":
             B.nvfp4_group_cast(x(), SPLITS, **out)
         elif entry == "quantize":
             B.nvfp4_group_quantize(x(), SPLITS, **out)
+        elif entry == "cast_4over6":
+            B.nvfp4_group_cast_4over6(x(), SPLITS, **out, scale_bound=256, err_mode=B.ERR_MSE)
+        elif entry == "cast_4over6_graphsafe":
+            B.nvfp4_group_cast_4over6_graphsafe(x(), E, offs, status, **out, scale_bound=256, err_mode=B.ERR_MAE)
         else:
             B.nvfp4_group_quantize_graphsafe(x(), E, torch.tensor([128, 256], dtype=torch.int32),
                                              torch.zeros(1, dtype=torch.int32), **out)
