@@ -17,7 +17,7 @@
 // Design: the grouped cast's tiles (128 x 256, one expert per tile, XCD-aware
 // order), lane layout (lane = 16 rows x 8 columns), staged rowwise lines and
 // scales, and streaming transposed stores.  The difference is arithmetic:
-// per block two scale steps with IEEE divisions and, per element and
+// per block two scale steps with correctly rounded quotients and, per element and
 // candidate, the code, its dequantised value and the error term -- about
 // fifteen VALU operations per element and direction, so the kernel is bound
 // by the vector ALUs rather than by HBM.
@@ -40,20 +40,21 @@ namespace {
 
 using namespace nvfp4g;
 
-// The two candidates' divisors.
-constexpr float kK6 = 6.0f;
-constexpr float kK4 = 4.0f;
-
-// One candidate's block step with IEEE divisions, in the order of the
-// method: t = (b / k) / s, S = E4M3(t), d = value(S) * s, m = 1 / d (0 when
-// d == 0, at most FLT_MAX).  Returns S; *sv = value(S).
-__device__ __forceinline__ uint32_t cand_step(float b, float kdiv, float s, float* sv, float* m) {
-  const float t = (s == 0.0f) ? 0.0f : (b / kdiv) / s;
+// One candidate's block step, in the order of the method: t = (u_k) / s with
+// u_k = b / k, S = E4M3(t), d = value(S) * s, m = 1 / d (0 when d == 0, at
+// most FLT_MAX).  Returns S; *sv = value(S).  Every quotient is the
+// correctly rounded one: b / 6 by div6_bf16 (b is a bf16 value), b / 4 is
+// exact, t by the IEEE division, and 1 / d by rcp_rn where d and 1 / d are
+// normal (the IEEE division elsewhere) -- the fast forms equal the IEEE
+// divisions on every input they are given (exhaustive GPU self-tests).
+__device__ __forceinline__ uint32_t cand_step(float u, float s, float* sv, float* m) {
+  const float t = (s == 0.0f) ? 0.0f : u / s;
   const uint32_t S = e4m3_code(t);
   const float v = e4m3_value(S);
   const float d = v * s;
   *sv = v;
-  *m = (d == 0.0f) ? 0.0f : fminf(1.0f / d, FLT_MAX);
+  const bool fast = d >= 0x1p-126f && d < 0x1p126f;
+  *m = (d == 0.0f) ? 0.0f : (fast ? rcp_rn(d) : fminf(1.0f / d, FLT_MAX));
   return S;
 }
 
@@ -109,8 +110,8 @@ __device__ __forceinline__ float block_err(const float (&x)[16], uint32_t c_lo, 
 template <int MODE>
 __device__ __forceinline__ uint32_t block_4o6(const float (&x)[16], float b, float s, uint32_t* lo, uint32_t* hi) {
   float sv6, m6, sv4, m4;
-  const uint32_t S6 = cand_step(b, kK6, s, &sv6, &m6);
-  const uint32_t S4 = cand_step(b, kK4, s, &sv4, &m4);
+  const uint32_t S6 = cand_step(div6_bf16(b), s, &sv6, &m6);
+  const uint32_t S4 = cand_step(b * 0.25f, s, &sv4, &m4);
   const uint32_t c6_lo = encode8f(x, m6), c6_hi = encode8f(x + 8, m6);
   const uint32_t c4_lo = encode8f(x, m4), c4_hi = encode8f(x + 8, m4);
   const float e6 = block_err<MODE>(x, c6_lo, c6_hi, sv6, s);

@@ -131,6 +131,23 @@ __device__ __forceinline__ uint32_t block_step(float b, float s, float ys, float
   return block_scale(b, s, m);
 }
 
+// RN(1/d) for 2^-126 <= d < 2^126 (d and 1/d normal): the hardware
+// reciprocal plus one Newton step.  On the hardware it equals the IEEE
+// division 1/d on every fp32 d in that range (GPU self-test).
+__device__ __forceinline__ float rcp_rn(float d) {
+  const float y0 = __builtin_amdgcn_rcpf(d);
+  return __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
+}
+
+// RN(b/6) for a bf16 value b >= 0 (given as fp32): b * RN(1/6) plus one
+// residual correction.  Equals the IEEE division b/6 on every finite
+// non-negative bf16 value (GPU self-test).
+__device__ __forceinline__ float div6_bf16(float b) {
+  const float r6 = 0x1.555556p-3f;  // RN(1/6)
+  const float q0 = b * r6;
+  return __builtin_fmaf(__builtin_fmaf(-6.0f, q0, b), r6, q0);
+}
+
 // Hardware FP4 conversion (gfx950): two fp32 values -> one E2M1x2 byte
 // (first value in the low nibble) placed at byte SEL of `old`.  With scale
 // 1.0 it rounds to nearest (ties to the even code), saturates at +-6 and

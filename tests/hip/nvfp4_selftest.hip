@@ -11,6 +11,9 @@
 //    bf16 values b <= A (b = block amax, A = line amax);
 //  * the hardware FP4 -> fp32 convert with unit scale (the four-over-six
 //    cast's dequantised values) on every byte at every byte position;
+//  * the fast reciprocal (rcp_rn) against the IEEE division on every normal
+//    fp32 d with a normal reciprocal, and the fast b/6 (div6_bf16) on every
+//    finite non-negative bf16 b;
 //  * sample outputs (block step, FP4 codes) that the tests compare with the
 //    CPU oracle.
 #include <hip/hip_runtime.h>
@@ -126,6 +129,28 @@ __global__ void fp4_decode_kernel(float* out) {
   out[2 * t + 1] = hi;
 }
 
+// d over every fp32 pattern in [2^-126, 2^126)
+__global__ void rcp_exhaustive_kernel(unsigned long long* counts) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  unsigned long long n = 0, bad = 0;
+  for (uint32_t p = 0x00800000u + blockIdx.x * blockDim.x + threadIdx.x; p < 0x7E800000u; p += stride) {
+    const float d = __uint_as_float(p);
+    n++;
+    bad += __float_as_uint(rcp_rn(d)) != __float_as_uint(1.0f / d);
+  }
+  atomicAdd(&counts[0], n);
+  atomicAdd(&counts[1], bad);
+}
+
+// b over every finite non-negative bf16 pattern (0 .. 0x7F7F)
+__global__ void div6_exhaustive_kernel(unsigned long long* counts) {
+  const uint32_t b16 = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b16 > 0x7F7Fu) return;
+  const float b = __uint_as_float(b16 << 16);
+  atomicAdd(&counts[0], 1ull);
+  if (__float_as_uint(div6_bf16(b)) != __float_as_uint(b / 6.0f)) atomicAdd(&counts[1], 1ull);
+}
+
 int status() { return hipGetLastError() == hipSuccess ? 0 : -4; }
 
 }  // namespace
@@ -164,6 +189,16 @@ int selftest_block_step_sample(const uint16_t* b16, const uint16_t* A16, int64_t
 int selftest_fp4_codes(const float* v, int64_t n, uint8_t* codes) {
   if (n <= 0) return 0;
   hipLaunchKernelGGL(fp4_codes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, 0, v, n, codes);
+  return status();
+}
+
+// counts (device, 2 x u64, zeroed by the caller): values, mismatches.
+int selftest_rcp_exhaustive(unsigned long long* counts) {
+  hipLaunchKernelGGL(rcp_exhaustive_kernel, dim3(4096), dim3(256), 0, 0, counts);
+  return status();
+}
+int selftest_div6_exhaustive(unsigned long long* counts) {
+  hipLaunchKernelGGL(div6_exhaustive_kernel, dim3(128), dim3(256), 0, 0, counts);
   return status();
 }
 

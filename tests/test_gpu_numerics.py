@@ -43,6 +43,8 @@ def lib():
     L.selftest_block_step_sample.argtypes = [P, P, ctypes.c_int64, P, P]
     L.selftest_fp4_codes.argtypes = [P, ctypes.c_int64, P]
     L.selftest_fp4_decode.argtypes = [P]
+    L.selftest_rcp_exhaustive.argtypes = [P]
+    L.selftest_div6_exhaustive.argtypes = [P]
     return L
 
 
@@ -142,3 +144,27 @@ def test_fp4_decode_equals_e2m1_values(lib):
         for sel in range(4):
             assert got[byte, sel, 0] == val[byte & 15], (byte, sel)
             assert got[byte, sel, 1] == val[byte >> 4], (byte, sel)
+
+
+def test_fast_reciprocal_equals_ieee_on_every_normal_d(lib):
+    """rcp_rn (hardware reciprocal + one Newton step) gives the IEEE 1/d on
+    every fp32 d in [2^-126, 2^126): the four-over-six cast uses it for the
+    element multiplier when its block's d lies in that range."""
+    log("fast reciprocal vs IEEE division, 2^31 - 2^24 - ... values")
+    c = torch.zeros(2, dtype=torch.int64, device="cuda:0")
+    assert lib.selftest_rcp_exhaustive(ptr(c)) == 0
+    torch.cuda.synchronize()
+    n, bad = c.tolist()
+    assert n == 0x7E800000 - 0x00800000
+    assert bad == 0, f"{bad} mismatches"
+
+
+def test_fast_div6_equals_ieee_on_every_bf16(lib):
+    """div6_bf16 gives the IEEE b/6 on every finite non-negative bf16 b
+    (subnormals and zero included)."""
+    c = torch.zeros(2, dtype=torch.int64, device="cuda:0")
+    assert lib.selftest_div6_exhaustive(ptr(c)) == 0
+    torch.cuda.synchronize()
+    n, bad = c.tolist()
+    assert n == 0x7F80
+    assert bad == 0, f"{bad} mismatches"
