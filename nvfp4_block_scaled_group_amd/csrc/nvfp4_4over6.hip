@@ -17,10 +17,11 @@
 // Design: the grouped cast's tiles (128 x 256, one expert per tile, XCD-aware
 // order), lane layout (lane = 16 rows x 8 columns), staged rowwise lines and
 // scales, and streaming transposed stores.  The difference is arithmetic:
-// per block two scale steps with correctly rounded quotients and, per element and
-// candidate, the code, its dequantised value and the error term -- about
-// fifteen VALU operations per element and direction, so the kernel is bound
-// by the vector ALUs rather than by HBM.
+// per block two scale steps (fast quotients proved to give what the IEEE
+// divisions give on every input they get) and, per element and candidate,
+// the code, its dequantised value and the error term -- about fifteen VALU
+// operations per element and direction, so the kernel is bound by the
+// vector ALUs rather than by HBM.
 //  * Columnwise blocks lie in one lane (16 rows of one column): both error
 //    sums run in the lane in row order.
 //  * Rowwise blocks are split over the lane pair (L, L^8) (8 columns each).
@@ -40,15 +41,16 @@ namespace {
 
 using namespace nvfp4g;
 
-// One candidate's block step, in the order of the method: t = (u_k) / s with
+// One candidate's block step, in the order of the method: t = u_k / s with
 // u_k = b / k, S = E4M3(t), d = value(S) * s, m = 1 / d (0 when d == 0, at
-// most FLT_MAX).  Returns S; *sv = value(S).  Every quotient is the
-// correctly rounded one: b / 6 by div6_bf16 (b is a bf16 value), b / 4 is
-// exact, t by the IEEE division, and 1 / d by rcp_rn where d and 1 / d are
-// normal (the IEEE division elsewhere) -- the fast forms equal the IEEE
-// divisions on every input they are given (exhaustive GPU self-tests).
-__device__ __forceinline__ uint32_t cand_step(float u, float s, float* sv, float* m) {
-  const float t = (s == 0.0f) ? 0.0f : u / s;
+// most FLT_MAX).  Returns S; *sv = value(S).  The fast forms give what the
+// IEEE divisions give on every input they are used for (exhaustive GPU
+// self-tests): b / 6 by div6_bf16 (b is a bf16 value; b / 4 is exact), the
+// E4M3 code of t by quot_fast with ys = RN(1/s) on lines with s >= 2^-112,
+// and 1 / d by rcp_rn where d and 1 / d are normal; the IEEE division
+// elsewhere.
+__device__ __forceinline__ uint32_t cand_step(float u, float s, float ys, float* sv, float* m) {
+  const float t = (s >= kFastMinLineScale) ? quot_fast(u, s, ys) : ((s == 0.0f) ? 0.0f : u / s);
   const uint32_t S = e4m3_code(t);
   const float v = e4m3_value(S);
   const float d = v * s;
@@ -104,14 +106,15 @@ __device__ __forceinline__ float block_err(const float (&x)[16], uint32_t c_lo, 
 }
 
 // Four-over-six step of one block of 16 values x (element order) with block
-// amax b on a line with scale s: both candidates, the one with the smaller
+// amax b on a line with scale sl.x (sl.y = RN(1/sl.x)): both candidates, the one with the smaller
 // error kept (6 on a tie).  Returns its scale code; *lo, *hi = its codes of
 // elements 0-7 and 8-15 (element 2j in the low nibble of byte j).
 template <int MODE>
-__device__ __forceinline__ uint32_t block_4o6(const float (&x)[16], float b, float s, uint32_t* lo, uint32_t* hi) {
+__device__ __forceinline__ uint32_t block_4o6(const float (&x)[16], float b, float2 sl, uint32_t* lo, uint32_t* hi) {
+  const float s = sl.x;
   float sv6, m6, sv4, m4;
-  const uint32_t S6 = cand_step(div6_bf16(b), s, &sv6, &m6);
-  const uint32_t S4 = cand_step(b * 0.25f, s, &sv4, &m4);
+  const uint32_t S6 = cand_step(div6_bf16(b), s, sl.y, &sv6, &m6);
+  const uint32_t S4 = cand_step(b * 0.25f, s, sl.y, &sv4, &m4);
   const uint32_t c6_lo = encode8f(x, m6), c6_hi = encode8f(x + 8, m6);
   const uint32_t c4_lo = encode8f(x, m4), c4_hi = encode8f(x + 8, m4);
   const float e6 = block_err<MODE>(x, c6_lo, c6_hi, sv6, s);
@@ -135,8 +138,8 @@ __global__ __launch_bounds__(kThreads) void group_cast_4o6_kernel(
     const uint16_t* __restrict__ x, int64_t k, Routing R, uint32_t nrow_tiles, float line_div, const float* __restrict__ row_amax, const float* __restrict__ col_amax,
     uint8_t* __restrict__ row_data, uint8_t* __restrict__ row_scale, uint8_t* __restrict__ col_data,
     uint8_t* __restrict__ col_scale) {
-  __shared__ float l_row[kTileRows];  // line scale per row of the tile
-  __shared__ float l_col[kTileCols];  // line scale per column of the tile
+  __shared__ float2 l_row[kTileRows];  // (s, 1/s) per row of the tile
+  __shared__ float2 l_col[kTileCols];  // (s, 1/s) per column of the tile
   __shared__ StagedRowScales l_rs;
   __shared__ StagedColScales l_cs;
   __shared__ StagedRowData l_rd;
@@ -164,8 +167,14 @@ __global__ __launch_bounds__(kThreads) void group_cast_4o6_kernel(
   const float a_col = col_data && (uint32_t)tid < ncols ? col_amax[(int64_t)e * k + col_base + tid] : 0.0f;
   uint32_t v[16][4];
   load_tile(x + (int64_t)row0 * k + col_base, ku, vo_x, v);
-  if (row_data && tid < kTileRows) l_row[tid] = a_row / line_div;
-  if (col_data) l_col[tid] = a_col / line_div;
+  if (row_data && tid < kTileRows) {
+    const float s = a_row / line_div;
+    l_row[tid] = make_float2(s, 1.0f / s);
+  }
+  if (col_data) {
+    const float s = a_col / line_div;
+    l_col[tid] = make_float2(s, 1.0f / s);
+  }
   __syncthreads();
 
   if (row_data) {

@@ -148,6 +148,16 @@ __device__ __forceinline__ float div6_bf16(float b) {
   return __builtin_fmaf(__builtin_fmaf(-6.0f, q0, b), r6, q0);
 }
 
+// u / s as u * ys plus one fused residual correction, given ys = RN(1/s)
+// (once per line).  For the four-over-six block steps -- s = A / (6 * Bnd)
+// with A a bf16 line amax, s >= 2^-112, Bnd in 1 .. 448, u = RN(b / 6) or
+// b / 4 for every bf16 block amax b <= A -- it gives the IEEE quotient's
+// E4M3 code on every input (exhaustive GPU self-test).
+__device__ __forceinline__ float quot_fast(float u, float s, float ys) {
+  const float t0 = u * ys;
+  return __builtin_fmaf(__builtin_fmaf(-s, t0, u), ys, t0);
+}
+
 // Hardware FP4 conversion (gfx950): two fp32 values -> one E2M1x2 byte
 // (first value in the low nibble) placed at byte SEL of `old`.  With scale
 // 1.0 it rounds to nearest (ties to the even code), saturates at +-6 and

@@ -14,6 +14,8 @@
 //  * the fast reciprocal (rcp_rn) against the IEEE division on every normal
 //    fp32 d with a normal reciprocal, and the fast b/6 (div6_bf16) on every
 //    finite non-negative bf16 b;
+//  * the fast quotient of the four-over-six block step (quot_fast) against
+//    the IEEE division on every (A, bound, b, candidate) it is used for;
 //  * sample outputs (block step, FP4 codes) that the tests compare with the
 //    CPU oracle.
 #include <hip/hip_runtime.h>
@@ -151,6 +153,34 @@ __global__ void div6_exhaustive_kernel(unsigned long long* counts) {
   if (__float_as_uint(div6_bf16(b)) != __float_as_uint(b / 6.0f)) atomicAdd(&counts[1], 1ull);
 }
 
+// one work-group per (line amax A = bf16 pattern 1..0x7F7F, bound 1..448);
+// b over every bf16 pattern 0..A, both candidates (u = b/6 and b/4):
+// quot_fast against the IEEE quotient u/s, by bits and by E4M3 code.  Lines
+// with s < 2^-112 are skipped (they keep the IEEE division) and counted.
+__global__ void quot_4o6_exhaustive_kernel(unsigned long long* counts) {
+  const uint32_t A16 = 1u + blockIdx.x;
+  const float A = __uint_as_float(A16 << 16);
+  const float s = A / (6.0f * (float)(1u + blockIdx.y));
+  if (!(s >= 0x1p-112f)) {
+    if (threadIdx.x == 0) atomicAdd(&counts[3], 1ull);
+    return;
+  }
+  const float ys = 1.0f / s;
+  unsigned long long n = 0, badt = 0, badS = 0;
+  for (uint32_t b16 = threadIdx.x; b16 <= A16; b16 += blockDim.x) {
+    const float b = __uint_as_float(b16 << 16);
+    const float u6 = b / 6.0f, u4 = b * 0.25f;
+    const float e6 = u6 / s, f6 = quot_fast(u6, s, ys);
+    const float e4 = u4 / s, f4 = quot_fast(u4, s, ys);
+    n += 2;
+    badt += (__float_as_uint(e6) != __float_as_uint(f6)) + (__float_as_uint(e4) != __float_as_uint(f4));
+    badS += (e4m3_code(e6) != e4m3_code(f6)) + (e4m3_code(e4) != e4m3_code(f4));
+  }
+  atomicAdd(&counts[0], n);
+  atomicAdd(&counts[1], badt);
+  atomicAdd(&counts[2], badS);
+}
+
 int status() { return hipGetLastError() == hipSuccess ? 0 : -4; }
 
 }  // namespace
@@ -199,6 +229,13 @@ int selftest_rcp_exhaustive(unsigned long long* counts) {
 }
 int selftest_div6_exhaustive(unsigned long long* counts) {
   hipLaunchKernelGGL(div6_exhaustive_kernel, dim3(128), dim3(256), 0, 0, counts);
+  return status();
+}
+
+// counts (device, 4 x u64, zeroed by the caller): quotients checked, bit
+// mismatches, E4M3-code mismatches, (A, bound) lines skipped.
+int selftest_quot_4o6_exhaustive(unsigned long long* counts) {
+  hipLaunchKernelGGL(quot_4o6_exhaustive_kernel, dim3(0x7F7F, 448), dim3(256), 0, 0, counts);
   return status();
 }
 

@@ -45,6 +45,7 @@ def lib():
     L.selftest_fp4_decode.argtypes = [P]
     L.selftest_rcp_exhaustive.argtypes = [P]
     L.selftest_div6_exhaustive.argtypes = [P]
+    L.selftest_quot_4o6_exhaustive.argtypes = [P]
     return L
 
 
@@ -168,3 +169,20 @@ def test_fast_div6_equals_ieee_on_every_bf16(lib):
     n, bad = c.tolist()
     assert n == 0x7F80
     assert bad == 0, f"{bad} mismatches"
+
+
+def test_fast_quotient_gives_the_ieee_e4m3_code_on_every_4o6_input(lib):
+    """quot_fast (u * RN(1/s) plus one residual correction) against the IEEE
+    quotient u / s over every input of the four-over-six block step: every
+    bf16 line amax A and bound 1..448 with s = A / (6 * bound) >= 2^-112,
+    every bf16 block amax b <= A, both candidates (u = b/6, b/4).  The E4M3
+    code it yields must always be the IEEE quotient's (the bits may differ
+    where both round to the same code)."""
+    log("fast quotient vs IEEE division over (A, bound, b, candidate)")
+    c = torch.zeros(4, dtype=torch.int64, device="cuda:0")
+    assert lib.selftest_quot_4o6_exhaustive(ptr(c)) == 0
+    torch.cuda.synchronize()
+    n, badt, badS, skipped = c.tolist()
+    log(f"{n} quotients, {badt} differ in bits, {badS} in E4M3 code; {skipped} (A, bound) lines skipped")
+    assert n > 4 * 10 ** 11
+    assert badS == 0
