@@ -96,7 +96,12 @@ int nvfp4_group_amax(const uint16_t* x, int64_t sum_m, int64_t k,
  * per-token NVFP4 fprop recipe"; columnwise per-column amax from "Enable
  * NVFP4 row-scaled (per-token) backward for GroupedLinear").  Consumes the
  * amax vectors of nvfp4_group_amax and writes the rowwise and/or columnwise
- * FP4 data and E4M3 scales in the layouts above. */
+ * FP4 data and E4M3 scales in the layouts above.  The bytes follow the
+ * numerics above for amax vectors that nvfp4_group_amax wrote for the same
+ * x and routing (each line's max |x|, a bf16 value): the block steps use
+ * fast quotients that were checked against the IEEE divisions over exactly
+ * such inputs.  Other amax values give finite output that may differ from
+ * those numerics in a scale's last rounding. */
 int nvfp4_group_cast(const uint16_t* x, int64_t sum_m, int64_t k,
                      int32_t num_experts, const int64_t* h_splits,
                      const float* row_amax, const float* col_amax,
@@ -316,7 +321,9 @@ int nvfp4_group_gemm_wgrad_graphsafe(const uint8_t* a_col_data,
  * scale_bound: 1 .. NVFP4G_4O6_MAX_BOUND; err_mode: NVFP4G_4O6_ERR_MSE or
  * NVFP4G_4O6_ERR_MAE; anything else returns NVFP4G_EINVAL.  Amax inputs
  * (from nvfp4_group_amax), layouts, directions and the other arguments as
- * in nvfp4_group_cast.  x must be finite. */
+ * in nvfp4_group_cast, including its condition on the amax vectors (the
+ * fast quotients here were checked over every bf16 line amax, bound and
+ * block amax at most the line amax).  x must be finite. */
 #define NVFP4G_4O6_ERR_MSE 0
 #define NVFP4G_4O6_ERR_MAE 1
 #define NVFP4G_4O6_MAX_BOUND 448

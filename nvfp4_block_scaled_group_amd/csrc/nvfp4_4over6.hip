@@ -106,9 +106,10 @@ __device__ __forceinline__ float block_err(const float (&x)[16], uint32_t c_lo, 
 }
 
 // Four-over-six step of one block of 16 values x (element order) with block
-// amax b on a line with scale sl.x (sl.y = RN(1/sl.x)): both candidates, the one with the smaller
-// error kept (6 on a tie).  Returns its scale code; *lo, *hi = its codes of
-// elements 0-7 and 8-15 (element 2j in the low nibble of byte j).
+// amax b on a line with scale sl.x (sl.y = RN(1/sl.x)): both candidates,
+// the one with the smaller error kept (6 on a tie).  Returns its scale code;
+// *lo, *hi = its codes of elements 0-7 and 8-15 (element 2j in the low
+// nibble of byte j).
 template <int MODE>
 __device__ __forceinline__ uint32_t block_4o6(const float (&x)[16], float b, float2 sl, uint32_t* lo, uint32_t* hi) {
   const float s = sl.x;
@@ -135,8 +136,8 @@ __device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void group_cast_4o6_kernel(
-    const uint16_t* __restrict__ x, int64_t k, Routing R, uint32_t nrow_tiles, float line_div, const float* __restrict__ row_amax, const float* __restrict__ col_amax,
-    uint8_t* __restrict__ row_data, uint8_t* __restrict__ row_scale, uint8_t* __restrict__ col_data,
+    const uint16_t* __restrict__ x, int64_t k, Routing R, uint32_t nrow_tiles, float line_div,
+    const float* __restrict__ row_amax, const float* __restrict__ col_amax, uint8_t* __restrict__ row_data, uint8_t* __restrict__ row_scale, uint8_t* __restrict__ col_data,
     uint8_t* __restrict__ col_scale) {
   __shared__ float2 l_row[kTileRows];  // (s, 1/s) per row of the tile
   __shared__ float2 l_col[kTileCols];  // (s, 1/s) per column of the tile
