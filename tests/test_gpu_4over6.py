@@ -76,6 +76,36 @@ def test_one_direction(rowwise, columnwise):
     check(w, 256, B.ERR_MSE, rowwise, columnwise)
 
 
+@pytest.mark.parametrize("bound,mode", [(1, B.ERR_MSE), (256, B.ERR_MAE), (448, B.ERR_MSE)])
+def test_tiny_and_huge_lines(bound, mode):
+    """Lines whose scale steps leave the fast quotients' ranges: bf16
+    subnormals and tiny normals (line scale below 2^-112, d and 1/d beyond
+    the normal range), huge rows (d at or above 2^126, up to overflow, so
+    m = 0 and the errors overflow), and ordinary rows in between; the
+    columns mix all of them."""
+    rng = np.random.default_rng(51)
+    M, K = 384, 80
+    v = rng.standard_normal((M, K)).astype(np.float32)
+    row_exp = rng.integers(-133, -95, (M, 1)).astype(np.float32)
+    v = v * np.exp2(row_exp)
+    v[::7] *= np.float32(2.0 ** 60)           # ordinary rows
+    v[3::11] = (rng.standard_normal((len(range(3, M, 11)), K)) * 2.0 ** 120).astype(np.float32)  # huge rows
+    w = synth.Workload("tiny_huge", synth.f32_to_bf16_bits(v), np.array([128, 256], np.int64))
+    check(w, bound, mode)
+
+
+def test_huge_outlier_next_to_tiny_values():
+    """A huge value in each line with tiny values around it: most blocks get
+    subnormal or zero scales for both candidates."""
+    rng = np.random.default_rng(52)
+    M, K = 256, 64
+    v = (rng.standard_normal((M, K)) * 1e-6).astype(np.float32)
+    v[np.arange(M), rng.integers(0, K, M)] = np.float32(3e4)
+    w = synth.Workload("extremes", synth.f32_to_bf16_bits(v), np.array([256], np.int64))
+    for bound, mode in ((256, B.ERR_MSE), (7, B.ERR_MAE)):
+        check(w, bound, mode)
+
+
 def test_both_candidates_are_taken():
     """The parity above is only meaningful if blocks pick both encodings: on
     the normal workload about half of the blocks keep k = 4; with bound 448
