@@ -329,7 +329,7 @@ def main():
                          "rocprofv3 --pmc run can scale FETCH_SIZE / WRITE_SIZE by a copy of known size")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
