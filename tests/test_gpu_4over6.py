@@ -340,3 +340,27 @@ def test_column_limit_k_2_to_22():
         d, s = _line_ref(np.ascontiguousarray(w.x[:, c]), res["col_amax"][c], bound, mode)
         assert np.array_equal(res["col_data"][c * (m // 2):(c + 1) * (m // 2)], d), f"col_data column {c}"
         assert np.array_equal(res["col_scale"][c * (m // 16):(c + 1) * (m // 16)], s), f"col_scale column {c}"
+
+
+@pytest.mark.parametrize("offs,bits", [
+    ([256, 128, 384], B.NVFP4G_DEV_NONMONO),
+    ([256, 300, 384], B.NVFP4G_DEV_UNALIGNED),
+    ([256, 384, 1280], B.NVFP4G_DEV_OVERFLOW),
+])
+def test_graphsafe_rejects_bad_device_routing(offs, bits):
+    """Invalid device routing: the status bit is set and no output byte is
+    written (the amax buffers hold a prefill the cast would otherwise read)."""
+    log(f"4over6 bad device routing {offs}")
+    cap, k = 1024, 32
+    x = torch.zeros((cap, k), dtype=torch.int16, device="cuda:0")
+    o = alloc(cap, k, 3, True, True)
+    for g in o.values():
+        g.t.view(torch.uint8).fill_(0x33)
+    d_offs = torch.tensor(offs, dtype=torch.int32, device="cuda:0")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    B.nvfp4_group_cast_4over6_graphsafe(x, 3, d_offs, status, **tensors(o), scale_bound=256, err_mode=B.ERR_MSE)
+    torch.cuda.synchronize()
+    assert int(status.item()) & bits
+    assert_guards(o)
+    for key, g in o.items():
+        assert (g.numpy().view(np.uint8) == 0x33).all(), key
