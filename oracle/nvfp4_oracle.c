@@ -240,6 +240,36 @@ int oracle_group_amax(const uint16_t* x, int64_t sum_m, int64_t k, int32_t E,
   return ORACLE_OK;
 }
 
+/* ------------------------------------------------------ per-tensor amax
+ *
+ * The row_scaled knob of the four-over-six converter page ("[NVFP4 4over6]
+ * Add the grouped-experts four-over-six converter", Summary and Review pass)
+ * switches the per-row amax off; the per-token page ("Implement per-token
+ * NVFP4 fprop recipe", Description) describes the per-row amax as replacing
+ * a per-tensor one.  Reading taken: with row scaling off, every line of an
+ * expert takes the expert's tensor amax A_e = max |x| over all of its rows
+ * and columns (each expert's slice is the tensor its GEMM sees), written as
+ * the amax vectors the casts consume: row_amax[r] = A_e for every row r of
+ * expert e and col_amax[e*k + c] = A_e for every column c; an expert with no
+ * rows gets 0.  Either output may be NULL. */
+int oracle_group_amax_tensor(const uint16_t* x, int64_t sum_m, int64_t k, int32_t E,
+                             const int64_t* splits, float* row_amax, float* col_amax) {
+  int rc = check_args(sum_m, k, E, splits);
+  if (rc != ORACLE_OK) return rc;
+  int64_t r0 = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    float A = 0.0f;
+    for (int64_t r = r0; r < r0 + splits[e]; ++r)
+      for (int64_t c = 0; c < k; ++c) A = fmaxf(A, fabsf(bf16_value(x[r * k + c])));
+    if (row_amax)
+      for (int64_t r = r0; r < r0 + splits[e]; ++r) row_amax[r] = A;
+    if (col_amax)
+      for (int64_t c = 0; c < k; ++c) col_amax[(int64_t)e * k + c] = A;
+    r0 += splits[e];
+  }
+  return ORACLE_OK;
+}
+
 /* Rowwise cast of row r: k/2 data bytes and k/16 scales. */
 int oracle_cast_row(const uint16_t* x, int64_t k, int64_t r, float A,
                     uint8_t* data, uint8_t* scales) {

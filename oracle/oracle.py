@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_col_amax.argtypes = [_P, _I64, _I64, _I64, _I64]
         L.oracle_col_amax.restype = _F
         L.oracle_group_amax.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P]
+        L.oracle_group_amax_tensor.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P]
         L.oracle_cast_row.argtypes = [_P, _I64, _I64, _F, _P, _P]
         L.oracle_cast_col.argtypes = [_P, _I64, _I64, _I64, _I64, _F, _P, _P]
         L.oracle_group_cast.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P]
@@ -200,6 +201,19 @@ def group_amax(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool = T
     return ra, ca
 
 
+def group_amax_tensor(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool = True):
+    """Per-tensor amax (row scaling off): every line of expert e gets the
+    expert's max |x|; returned as the (row_amax, col_amax) vectors."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    sum_m, k = x.shape
+    sp = np.ascontiguousarray(splits, dtype=np.int64)
+    E = sp.size
+    ra = np.empty(sum_m, dtype=np.float32) if rowwise else None
+    ca = np.empty(E * k, dtype=np.float32) if columnwise else None
+    _check(lib().oracle_group_amax_tensor(_ptr(x), sum_m, k, E, _ptr(sp), _ptr(ra), _ptr(ca)), "group_amax_tensor")
+    return ra, ca
+
+
 def group_cast(x: np.ndarray, splits, row_amax=None, col_amax=None,
                rowwise: bool = True, columnwise: bool = True):
     """Grouped cast.  Returns (row_data, row_scale, col_data, col_scale); the
@@ -219,9 +233,10 @@ def group_cast(x: np.ndarray, splits, row_amax=None, col_amax=None,
     return rd, rs, cd, cs
 
 
-def group_quantize(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool = True):
-    """Amax then cast, as one dict of numpy arrays."""
-    ra, ca = group_amax(x, splits, rowwise, columnwise)
+def group_quantize(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool = True, row_scaled: bool = True):
+    """Amax (per line, or per expert tensor when row_scaled is False) then
+    cast, as one dict of numpy arrays."""
+    ra, ca = (group_amax if row_scaled else group_amax_tensor)(x, splits, rowwise, columnwise)
     rd, rs, cd, cs = group_cast(x, splits, ra, ca, rowwise, columnwise)
     return {"row_amax": ra, "col_amax": ca, "row_data": rd, "row_scale": rs,
             "col_data": cd, "col_scale": cs}
@@ -356,9 +371,10 @@ def group_cast_4o6(x: np.ndarray, splits, row_amax=None, col_amax=None, bound: i
 
 
 def group_quantize_4o6(x: np.ndarray, splits, bound: int = DEFAULT_4O6_BOUND, err_mode: int = ERR_MSE,
-                       rowwise: bool = True, columnwise: bool = True):
-    """Amax (the plain grouped amax) then the four-over-six cast."""
-    ra, ca = group_amax(x, splits, rowwise, columnwise)
+                       rowwise: bool = True, columnwise: bool = True, row_scaled: bool = True):
+    """Amax (per line, or per expert tensor when row_scaled is False) then
+    the four-over-six cast."""
+    ra, ca = (group_amax if row_scaled else group_amax_tensor)(x, splits, rowwise, columnwise)
     rd, rs, cd, cs = group_cast_4o6(x, splits, ra, ca, bound, err_mode, rowwise, columnwise)
     return {"row_amax": ra, "col_amax": ca, "row_data": rd, "row_scale": rs, "col_data": cd, "col_scale": cs}
 
