@@ -79,18 +79,30 @@ def alloc(sum_m: int, k: int, num_experts: int, rowwise: bool, columnwise: bool)
     return res
 
 
-def _call(x, splits, rowwise, columnwise, four_over_six):
+def _call(x, splits, rowwise, columnwise, four_over_six, amax=None):
+    """The oracle on one piece: amax + cast, or (with ``amax`` = the piece's
+    (row_amax, col_amax) slices of precomputed vectors) the cast alone."""
+    if amax is None:
+        if four_over_six is None:
+            return O.group_quantize(x, splits, rowwise, columnwise)
+        bound, err_mode = four_over_six
+        return O.group_quantize_4o6(x, splits, bound, err_mode, rowwise, columnwise)
+    ra, ca = amax
     if four_over_six is None:
-        return O.group_quantize(x, splits, rowwise, columnwise)
-    bound, err_mode = four_over_six
-    return O.group_quantize_4o6(x, splits, bound, err_mode, rowwise, columnwise)
+        rd, rs, cd, cs = O.group_cast(x, splits, ra, ca, rowwise, columnwise)
+    else:
+        rd, rs, cd, cs = O.group_cast_4o6(x, splits, ra, ca, four_over_six[0], four_over_six[1], rowwise, columnwise)
+    return {"row_amax": ra, "col_amax": ca, "row_data": rd, "row_scale": rs, "col_data": cd, "col_scale": cs}
 
 
-def run_task(x: np.ndarray, k: int, task, res: dict, four_over_six=None) -> None:
-    """One oracle call; its bytes go to their place in the whole outputs."""
+def run_task(x: np.ndarray, k: int, task, res: dict, four_over_six=None, amax=None) -> None:
+    """One oracle call; its bytes go to their place in the whole outputs.
+    ``amax`` = whole precomputed (row_amax, col_amax) vectors (per-tensor
+    scaling), sliced for the piece; otherwise the piece computes its own."""
     if task[0] == "row":
         _, r0, r1 = task
-        part = _call(x[r0:r1], [r1 - r0], True, False, four_over_six)
+        piece = None if amax is None else (amax[0][r0:r1], None)
+        part = _call(x[r0:r1], [r1 - r0], True, False, four_over_six, piece)
         res["row_amax"][r0:r1] = part["row_amax"]
         res["row_data"][r0:r1] = part["row_data"]
         res["row_scale"][r0:r1] = part["row_scale"]
@@ -98,7 +110,8 @@ def run_task(x: np.ndarray, k: int, task, res: dict, four_over_six=None) -> None
         _, e, lo, hi, c0, c1 = task
         m = hi - lo
         xs = np.ascontiguousarray(x[lo:hi, c0:c1])
-        part = _call(xs, [m], False, True, four_over_six)
+        piece = None if amax is None else (None, amax[1][e * k + c0:e * k + c1])
+        part = _call(xs, [m], False, True, four_over_six, piece)
         res["col_amax"][e * k + c0:e * k + c1] = part["col_amax"]
         res["col_data"][k * lo // 2 + c0 * (m // 2):k * lo // 2 + c1 * (m // 2)] = part["col_data"]
         res["col_scale"][k * lo // 16 + c0 * (m // 16):k * lo // 16 + c1 * (m // 16)] = part["col_scale"]
@@ -106,12 +119,15 @@ def run_task(x: np.ndarray, k: int, task, res: dict, four_over_six=None) -> None
 
 def group_quantize(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool = True,
                    threads: int | None = None, rows_per_task: int = ROWS_PER_TASK,
-                   cols_per_task: int = COLS_PER_TASK, four_over_six=None) -> dict:
+                   cols_per_task: int = COLS_PER_TASK, four_over_six=None, row_scaled: bool = True) -> dict:
     """The oracle's amax + cast of the whole packed buffer ``x`` (bf16 bits,
     (sum_m, k)), as one dict of numpy arrays (None for a direction not asked
     for).  ``four_over_six = (bound, err_mode)`` runs the oracle's
     four-over-six cast instead of the plain one (the pieces are independent
-    in the same way: a block's choice depends only on its line)."""
+    in the same way: a block's choice depends only on its line).
+    ``row_scaled=False``: the per-tensor amax (every line of an expert takes
+    the expert's max |x|) is computed first, in one oracle call, and each
+    piece casts with its slice of it."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     sum_m, k = x.shape
     sp = [int(v) for v in splits]
@@ -119,12 +135,16 @@ def group_quantize(x: np.ndarray, splits, rowwise: bool = True, columnwise: bool
         raise ValueError("splits must sum to the row count")
     res = alloc(sum_m, k, len(sp), rowwise, columnwise)
     work = tasks(sp, k, rowwise, columnwise, rows_per_task, cols_per_task)
+    amax = None
+    if not row_scaled:
+        ra, ca = O.group_amax_tensor(x, sp, True, True)
+        amax = (ra, ca)
     n = threads or default_threads()
     if n == 1:
         for t in work:
-            run_task(x, k, t, res, four_over_six)
+            run_task(x, k, t, res, four_over_six, amax)
     else:
         with ThreadPoolExecutor(max_workers=n) as pool:
-            for f in [pool.submit(run_task, x, k, t, res, four_over_six) for t in work]:
+            for f in [pool.submit(run_task, x, k, t, res, four_over_six, amax) for t in work]:
                 f.result()
     return res

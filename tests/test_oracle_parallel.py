@@ -54,3 +54,19 @@ def test_parallel_four_over_six_equals_one_call(bound, mode):
         if a.dtype == np.float32:
             a, b = a.view(np.uint32), b.view(np.uint32)
         assert np.array_equal(a.reshape(-1), b.reshape(-1)), key
+
+
+@pytest.mark.parametrize("four_over_six", [None, (256, 0), (448, 1)])
+def test_parallel_per_tensor_equals_one_call(four_over_six):
+    """Per-tensor scaling (row_scaled False): the pieces cast with slices of
+    the expert amax vectors computed once, giving the single call's bytes."""
+    w = synth.random_case(23, [256, 0, 384, 128], 96, "rowscale")
+    sp = [int(v) for v in w.splits]
+    if four_over_six is None:
+        ref = O.group_quantize(w.x, sp, row_scaled=False)
+    else:
+        ref = O.group_quantize_4o6(w.x, sp, four_over_six[0], four_over_six[1], row_scaled=False)
+    got = OP.group_quantize(w.x, sp, threads=3, rows_per_task=128, cols_per_task=32, four_over_six=four_over_six,
+                            row_scaled=False)
+    for key in ref:
+        assert np.array_equal(np.asarray(got[key]).reshape(-1), np.asarray(ref[key]).reshape(-1)), key
