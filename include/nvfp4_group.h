@@ -122,6 +122,32 @@ int nvfp4_group_amax_graphsafe(const uint16_t* x, int64_t m_capacity, int64_t k,
                                float* row_amax, float* col_amax,
                                int32_t* d_status, void* stream);
 
+/* Per-tensor amax, for casts with row scaling off: the row_scaled knob of
+ * the four-over-six converter page ("[NVFP4 4over6] Add the grouped-experts
+ * four-over-six converter", Summary and Review pass); the per-token page
+ * ("Implement per-token NVFP4 fprop recipe", Description) describes the
+ * per-row amax as replacing a per-tensor one.  Every line of expert e gets
+ * the expert's tensor amax A_e = max |x| over all of its rows and columns:
+ * row_amax[r] = A_e for each row r of expert e and col_amax[e*k + c] = A_e
+ * (0 for an expert with no rows).  The vectors feed nvfp4_group_cast and
+ * nvfp4_group_cast_4over6 unchanged, which then scale every line of an
+ * expert alike.  Arguments as in nvfp4_group_amax; either output may be
+ * NULL (at least one is needed for a result).  Runs the grouped amax and
+ * one more launch (one work-group per expert). */
+int nvfp4_group_amax_tensor(const uint16_t* x, int64_t sum_m, int64_t k,
+                            int32_t num_experts, const int64_t* h_splits,
+                            float* row_amax, float* col_amax, void* stream);
+
+/* Graph-safe form of nvfp4_group_amax_tensor (routing, buffers and status as
+ * in nvfp4_group_amax_graphsafe; rows at or beyond offs[E-1] are neither
+ * read nor written).  Output equals nvfp4_group_amax_tensor's for the same
+ * routing. */
+int nvfp4_group_amax_tensor_graphsafe(const uint16_t* x, int64_t m_capacity,
+                                      int64_t k, int32_t num_experts,
+                                      const int32_t* d_offs, float* row_amax,
+                                      float* col_amax, int32_t* d_status,
+                                      void* stream);
+
 /* Graph-safe grouped cast: as nvfp4_group_cast with the routing taken from
  * d_offs (see nvfp4_group_amax_graphsafe).  row_data/row_scale hold
  * m_capacity rows; col_data/col_scale hold k*m_capacity/2 and

@@ -42,6 +42,7 @@ EXPORTS = (
     "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
     "nvfp4_group_gemm", "nvfp4_group_gemm_graphsafe", "nvfp4_group_gemm_wgrad", "nvfp4_group_gemm_wgrad_graphsafe",
     "nvfp4_group_cast_4over6", "nvfp4_group_cast_4over6_graphsafe",
+    "nvfp4_group_amax_tensor", "nvfp4_group_amax_tensor_graphsafe",
     "nvfp4_group_strerror",
 )
 
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.nvfp4_group_gemm_graphsafe.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P]
     L.nvfp4_group_gemm_wgrad.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P]
     L.nvfp4_group_gemm_wgrad_graphsafe.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P]
+    L.nvfp4_group_amax_tensor.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P]
+    L.nvfp4_group_amax_tensor_graphsafe.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P]
     L.nvfp4_group_cast_4over6.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P]
     L.nvfp4_group_cast_4over6_graphsafe.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _P,
                                                     _P, _P]
@@ -239,6 +242,22 @@ def nvfp4_group_quantize_graphsafe(x, num_experts, d_offs, d_status, row_amax=No
     bufs = _outputs(m, k, e, row_amax, col_amax, row_data, row_scale, col_data, col_scale)
     _check("nvfp4_group_quantize_graphsafe", load_library().nvfp4_group_quantize_graphsafe(
         xp, m, k, e, do, *bufs, ds, _stream(stream)))
+
+
+def nvfp4_group_amax_tensor(x, h_splits, row_amax=None, col_amax=None, stream=None):
+    xp, m, k = _x(x)
+    sp, e = _splits(h_splits)
+    ra, ca = _buf("row_amax", row_amax, F32, m), _buf("col_amax", col_amax, F32, e * k)
+    _check("nvfp4_group_amax_tensor", load_library().nvfp4_group_amax_tensor(xp, m, k, e, sp, ra, ca, _stream(stream)))
+
+
+def nvfp4_group_amax_tensor_graphsafe(x, num_experts, d_offs, d_status, row_amax=None, col_amax=None, stream=None):
+    xp, m, k = _x(x)
+    e = int(num_experts)
+    do, ds = _routing(e, d_offs, d_status)
+    ra, ca = _buf("row_amax", row_amax, F32, m), _buf("col_amax", col_amax, F32, e * k)
+    _check("nvfp4_group_amax_tensor_graphsafe", load_library().nvfp4_group_amax_tensor_graphsafe(
+        xp, m, k, e, do, ra, ca, ds, _stream(stream)))
 
 
 def nvfp4_group_cast_4over6(x, h_splits, row_amax=None, col_amax=None, row_data=None, row_scale=None,

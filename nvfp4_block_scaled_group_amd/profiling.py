@@ -41,6 +41,7 @@ COPY_BYTES = 1 << 30
 KERNEL_SOURCES = {
     "mxfp4_group_cast_kernel": "mxfp4_group.hip",
     "group_cast_4o6_kernel": "nvfp4_4over6.hip",
+    "amax_tensor_kernel": "nvfp4_amax_tensor.hip",
     "group_cast_kernel": "nvfp4_group.hip",
     "group_amax_kernel": "nvfp4_group.hip",
     "group_amax_rows_kernel": "nvfp4_group.hip",

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
         "nvfp4_group_dequant_columnwise_graphsafe", "mxfp4_group_cast", "mxfp4_group_cast_graphsafe",
         "nvfp4_group_gemm", "nvfp4_group_gemm_graphsafe", "nvfp4_group_gemm_wgrad",
         "nvfp4_group_gemm_wgrad_graphsafe", "nvfp4_group_cast_4over6", "nvfp4_group_cast_4over6_graphsafe",
-        "nvfp4_group_strerror",
+        "nvfp4_group_amax_tensor", "nvfp4_group_amax_tensor_graphsafe", "nvfp4_group_strerror",
     }
 
 
