@@ -68,6 +68,14 @@ def test_bad_output_buffer_is_rejected(key, bad, entry):
                                              torch.zeros(1, dtype=torch.int32), **out)
 
 
+@pytest.mark.parametrize("fn", ["nvfp4_group_amax", "nvfp4_group_amax_tensor"])
+def test_amax_entries_check_their_buffers(fn):
+    with pytest.raises(ValueError, match="col_amax"):
+        getattr(B, fn)(x(), SPLITS, torch.zeros(M), torch.zeros(E * K - 1))
+    with pytest.raises(ValueError, match="row_amax"):
+        getattr(B, fn)(x(), SPLITS, torch.zeros(M - 1), None)
+
+
 def test_amax_buffers_checked():
     with pytest.raises(ValueError, match="col_amax"):
         B.nvfp4_group_amax(x(), SPLITS, torch.zeros(M), torch.zeros(E * K - 1))

@@ -236,3 +236,20 @@ def test_4over6_host_checks(lib):
     assert g(FAKE, 256, 32, 2, None, FAKE, None, 256, 0, *out, FAKE, None) == -1   # no device offsets
     assert g(FAKE, 256, 32, 2, FAKE, FAKE, None, 256, 0, *out, None, None) == -1   # no status word
     assert g(FAKE, 256, 32, 2, FAKE, FAKE, None, 1000, 0, *out, FAKE, None) == -1  # bound out of range
+
+
+def test_amax_tensor_host_checks(lib):
+    """The per-tensor amax runs the grouped amax's host checks first."""
+    f = lib.nvfp4_group_amax_tensor
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 4
+    sp = (ctypes.c_int64 * 2)(128, 100)
+    assert f(FAKE, 228, 32, 2, sp, FAKE, FAKE, None) == -2          # split not a multiple of 128
+    ok = (ctypes.c_int64 * 1)(128)
+    assert f(FAKE, 128, 24, 1, ok, FAKE, FAKE, None) == -1          # k not a multiple of 16
+    assert f(FAKE, 128, 32, 1, ok, FAKE + 2, None, None) == -3      # misaligned row amax
+    g = lib.nvfp4_group_amax_tensor_graphsafe
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 5
+    assert g(FAKE, 256, 32, 2, None, FAKE, FAKE, FAKE, None) == -1  # no device offsets
+    assert g(FAKE, 256, 32, 2, FAKE, FAKE, FAKE, None, None) == -1  # no status word
