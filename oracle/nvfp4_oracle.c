@@ -42,11 +42,19 @@
  * A "line" is a row of X (rowwise) or one column of one expert's rows
  * (columnwise); blocks are 16 consecutive elements of a line.
  *
+ * Further sections below: the MXFP4 sibling cast (OCP MX scale rule), the
+ * four-over-six block scaling (a reading of the recipe the torchtitan
+ * converter page names; the selection rule comes from the published method
+ * of that name, so its agreement with that method's own code is not
+ * pinned), and the per-tensor amax for casts with row scaling off.
+ *
  * Parity pins: every function here is pinned by the CPU tests (exhaustive
  * and special-case checks of the two conversions against their definitions
  * and against torch's float8_e4m3fn cast, closed-form round trips, an
  * independent numpy brute force, grouped == per-expert loop, the half-gap
- * error bound and hand-worked golden rows).  No function is left unpinned.
+ * error bound, hand-worked golden rows, and mutations of the oracle that the
+ * pins must catch).  No function is left unpinned against its own
+ * definition.
  */
 #include <float.h>
 #include <math.h>
