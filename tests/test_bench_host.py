@@ -92,3 +92,48 @@ def test_committed_summaries_parse(name):
     cast = data["kernels"]["group_cast_kernel"]
     assert cast["fetch_bytes"] > 0 and cast["write_bytes"] > 0
     assert np.isclose(data["fetch_scale"], 2.0, rtol=0.01) and np.isclose(data["write_scale"], 1.0, rtol=0.01)
+
+
+def test_four_over_six_row_accounting():
+    """The four-over-six bench row: the cast kernel's byte count and the
+    method's fp32 operation count (6 per element, candidate and direction)
+    against the non-packed VALU issue rate (256 CUs x 4 SIMDs x 16 lanes x
+    2.4 GHz), with the library replaced by a stand-in that records calls."""
+    import torch
+
+    calls = []
+
+    class FakeB:
+        DEFAULT_4O6_BOUND, ERR_MSE, ERR_MAE = 256, 0, 1
+
+        @staticmethod
+        def alloc_outputs(m, k, e, device=None):
+            from nvfp4_block_scaled_group_amd import binding
+            return binding.alloc_outputs(m, k, e, device="cpu")
+
+        @staticmethod
+        def nvfp4_group_cast_4over6(x, splits, **kw):
+            calls.append((kw["scale_bound"], kw["err_mode"]))
+
+    m, k, E = 256, 64, 2
+    x = torch.zeros((m, k), dtype=torch.int16)
+    out = FakeB.alloc_outputs(m, k, E)
+
+    def timed(fn):
+        fn()
+        return 1e-5  # ms: 24 * 16384 operations at ~39 T/s
+
+    def entry(kernel, ms, nbytes):
+        return {"kernel": kernel, "ms": ms, "bytes": nbytes}
+
+    res = bench.four_over_six_rows(FakeB, torch, timed, entry, x, [128, 128], out, E, k, m)
+    assert calls == [(256, 0), (256, 1)]
+    N = m * k
+    for tag in ("mse", "mae"):
+        r = res[f"nvfp4_group_cast_4over6_{tag}"]
+        assert r["bytes"] == bench.algorithmic_bytes(m, k, E, True, True)["cast_kernel"]
+        alu = r["alu"]
+        assert alu["method_fp32_ops_per_launch"] == 24 * N
+        assert alu["peak_Tops"] == pytest.approx(39.3216)
+        assert alu["achieved_Tops"] == pytest.approx(24 * N / 1e-8 / 1e12, rel=1e-3)
+        assert alu["frac"] == pytest.approx(24 * N / 1e-8 / 1e12 / 39.3216, rel=1e-3)
