@@ -66,10 +66,13 @@ def _code(text: str) -> str:
 def source_sha256(kernel: str) -> str:
     """SHA-256 over the code of the kernel's .hip file, the shared headers,
     the C ABI header (its macros set sizes the kernels use) and the compiler
-    flags the library is built with (a -D or -O change changes the code)."""
+    flags the library is built with (a -D or -O change changes the code; the
+    include paths, which depend on where the repository sits, are left out)."""
     from . import build
     h = hashlib.sha256()
-    h.update(("flags\0" + " ".join(build.HIPCC_FLAGS) + "\0").encode())
+    # include paths name where the repository sits, not what is compiled
+    flags = [f for f in build.HIPCC_FLAGS if not f.startswith("-I")]
+    h.update(("flags\0" + " ".join(flags) + "\0").encode())
     files = [KERNEL_SOURCES[kernel]] + sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
     paths = [os.path.join(CSRC, f) for f in files] + [ABI_HEADER]
     for path in paths:

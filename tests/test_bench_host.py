@@ -65,6 +65,16 @@ def test_code_hash_covers_the_build_flags(monkeypatch):
     assert profiling.source_sha256("group_cast_kernel") != before
 
 
+def test_code_hash_does_not_depend_on_where_the_repository_sits(monkeypatch):
+    """The GPU host runs a copy of the repository at another path: the hash
+    of the same code must not change with the include path's location."""
+    from nvfp4_block_scaled_group_amd import build
+    before = profiling.source_sha256("group_cast_kernel")
+    moved = [("-I/elsewhere/include" if f.startswith("-I") else f) for f in build.HIPCC_FLAGS]
+    monkeypatch.setattr(build, "HIPCC_FLAGS", moved)
+    assert profiling.source_sha256("group_cast_kernel") == before
+
+
 def _summary(tmp_path, sha):
     data = {"workload": "w", "fetch_scale": 2.0, "write_scale": 1.0,
             "kernels": {"group_cast_kernel": {"fetch_bytes": 10, "write_bytes": 5, "source_sha256": sha}}}
