@@ -36,21 +36,28 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ABI_HEADER = os.path.join(os.path.dirname(PKG), "include", "nvfp4_group.h")
 COPY_BYTES = 1 << 30
-# kernel -> the .hip file that defines it; the longer names come first, since
-# names are matched as substrings of the profiler's kernel names
+# kernel -> the .hip file that defines it (relative to the package); the
+# longer names come first, since names are matched as substrings of the
+# profiler's kernel names.  The probe kernels are the memory-ceiling kernels
+# the benchmark times beside the library's.
 KERNEL_SOURCES = {
-    "mxfp4_group_cast_kernel": "mxfp4_group.hip",
-    "group_cast_4o6_kernel": "nvfp4_4over6.hip",
-    "amax_tensor_kernel": "nvfp4_amax_tensor.hip",
-    "group_cast_kernel": "nvfp4_group.hip",
-    "group_amax_kernel": "nvfp4_group.hip",
-    "group_amax_rows_kernel": "nvfp4_group.hip",
-    "amax_init_kernel": "nvfp4_group.hip",
-    "group_quantize_rowwise_kernel": "nvfp4_group.hip",
-    "group_quantize_small_kernel": "nvfp4_group.hip",
-    "dequant_kernel": "nvfp4_dequant.hip",
-    "gemm_fwd_kernel": "nvfp4_gemm.hip",
-    "gemm_wgrad_kernel": "nvfp4_gemm.hip",
+    "mxfp4_group_cast_kernel": "csrc/mxfp4_group.hip",
+    "group_cast_4o6_kernel": "csrc/nvfp4_4over6.hip",
+    "amax_tensor_kernel": "csrc/nvfp4_amax_tensor.hip",
+    "group_cast_kernel": "csrc/nvfp4_group.hip",
+    "group_amax_kernel": "csrc/nvfp4_group.hip",
+    "group_amax_rows_kernel": "csrc/nvfp4_group.hip",
+    "amax_init_kernel": "csrc/nvfp4_group.hip",
+    "group_quantize_rowwise_kernel": "csrc/nvfp4_group.hip",
+    "group_quantize_small_kernel": "csrc/nvfp4_group.hip",
+    "dequant_kernel": "csrc/nvfp4_dequant.hip",
+    "gemm_fwd_kernel": "csrc/nvfp4_gemm.hip",
+    "gemm_wgrad_kernel": "csrc/nvfp4_gemm.hip",
+    "cast_pattern_kernel": "probe/hbm_probe.hip",
+    "read_kernel": "probe/hbm_probe.hip",
+    "fill_kernel": "probe/hbm_probe.hip",
+    "copy_kernel": "probe/hbm_probe.hip",
+    "mix_kernel": "probe/hbm_probe.hip",
 }
 KERNELS = tuple(KERNEL_SOURCES)
 
@@ -73,8 +80,8 @@ def source_sha256(kernel: str) -> str:
     # include paths name where the repository sits, not what is compiled
     flags = [f for f in build.HIPCC_FLAGS if not f.startswith("-I")]
     h.update(("flags\0" + " ".join(flags) + "\0").encode())
-    files = [KERNEL_SOURCES[kernel]] + sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
-    paths = [os.path.join(CSRC, f) for f in files] + [ABI_HEADER]
+    paths = ([os.path.join(PKG, KERNEL_SOURCES[kernel])] +
+             [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".hpp")] + [ABI_HEADER])
     for path in paths:
         with open(path) as f:
             h.update(os.path.basename(path).encode() + b"\0" + _code(f.read()).encode())

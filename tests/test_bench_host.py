@@ -75,6 +75,21 @@ def test_code_hash_does_not_depend_on_where_the_repository_sits(monkeypatch):
     assert profiling.source_sha256("group_cast_kernel") == before
 
 
+def test_every_profiled_kernel_names_an_existing_source():
+    """Each kernel the summaries can list maps to a source file that exists
+    (the library's kernels under csrc/, the memory-ceiling kernels under
+    probe/), and kernels of one file share its hash."""
+    for k, rel in profiling.KERNEL_SOURCES.items():
+        assert os.path.isfile(os.path.join(profiling.PKG, rel)), (k, rel)
+        assert len(profiling.source_sha256(k)) == 64
+    assert profiling.source_sha256("copy_kernel") == profiling.source_sha256("read_kernel")
+    assert profiling.source_sha256("copy_kernel") != profiling.source_sha256("group_cast_kernel")
+    # the longer names are matched first
+    assert profiling._short("(anonymous namespace)::group_cast_4o6_kernel<0>(...)") == "group_cast_4o6_kernel"
+    assert profiling._short("(anonymous namespace)::cast_pattern_kernel(...)") == "cast_pattern_kernel"
+    assert profiling._short("__amd_rocclr_copyBuffer") == "copy"
+
+
 def _summary(tmp_path, sha):
     data = {"workload": "w", "fetch_scale": 2.0, "write_scale": 1.0,
             "kernels": {"group_cast_kernel": {"fetch_bytes": 10, "write_bytes": 5, "source_sha256": sha}}}
