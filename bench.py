@@ -60,7 +60,9 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "grouped NVFP4 amax+cast HBM GB/s (bytes in+out) and % of MI355X peak BW"
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, per workload
 TRAFFIC_FILES = {"deepseek_share": "profiles/group_cast_kernel-deepseek_share_e32_k7168_m65536.md",
-                 "down_proj": "profiles/group_cast_kernel-down_proj_e64_k2048_m131072.md"}
+                 "down_proj": "profiles/group_cast_kernel-down_proj_e64_k2048_m131072.md",
+                 "tiny": "profiles/group_quantize_small_kernel-tiny_e4_k256_m512.md",
+                 "outliers": "profiles/group_quantize_rowwise_kernel-outliers_e8_k2048_m8192_rowwise.md"}
 
 
 class TimingEvents:

@@ -593,7 +593,14 @@ __global__ __launch_bounds__(kSmallThreads) void group_quantize_small_kernel(
   __shared__ uint16_t l_ra[kSmallMaxRows];              // row amax (bf16 bits)
   __shared__ uint32_t l_cp[kSmallThreads];              // column maxima: partial, then final pairs
   if (!routing_ok(R)) return;
-  const int e = blockIdx.x / kSmallSplit, g = blockIdx.x % kSmallSplit;
+  // The kSmallSplit work-groups of an expert share one XCD (work-groups are
+  // dealt to the XCDs round-robin by index): the expert's rows then come
+  // from HBM once and from that XCD's L2 for the others.  Indexes past the
+  // last expert (E not a multiple of kNumXcd) exit.
+  const uint32_t L = blockIdx.x;
+  const int e = (int)(kNumXcd * (L / (kNumXcd * kSmallSplit)) + L % kNumXcd);
+  const int g = (int)((L / kNumXcd) % kSmallSplit);
+  if (e >= R.num_experts) return;
   const int32_t rend = route_end(R, e), rbeg = e ? route_end(R, e - 1) : 0;
   const uint32_t me = (uint32_t)(rend - rbeg);
   const int tid = threadIdx.x;
@@ -800,7 +807,8 @@ int64_t max_expert_rows(const Routing& R) {
 
 int launch_small(const uint16_t* x, int64_t k, const Routing& R, float* row_amax, float* col_amax,
                  uint8_t* row_data, uint8_t* row_scale, uint8_t* col_data, uint8_t* col_scale, hipStream_t st) {
-  hipLaunchKernelGGL(group_quantize_small_kernel, dim3((unsigned)R.num_experts * kSmallSplit), dim3(kSmallThreads), 0, st, x,
+  const unsigned groups = (unsigned)((R.num_experts + kNumXcd - 1) / kNumXcd);  // of kNumXcd experts
+  hipLaunchKernelGGL(group_quantize_small_kernel, dim3(groups * kNumXcd * kSmallSplit), dim3(kSmallThreads), 0, st, x,
                      k, R, row_data ? row_amax : nullptr, col_amax, row_data, row_scale, col_data, col_scale);
   return hip_status();
 }

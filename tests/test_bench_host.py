@@ -107,16 +107,32 @@ def test_traffic_is_read_only_for_the_current_code(tmp_path):
     assert profiling.load_traffic(str(tmp_path / "missing.md"), "group_cast_kernel") is None
 
 
-@pytest.mark.parametrize("name", ["profiles/group_cast_kernel-deepseek_share_e32_k7168_m65536.md",
-                                  "profiles/group_cast_kernel-down_proj_e64_k2048_m131072.md"])
-def test_committed_summaries_parse(name):
-    # each summary names the command that made it and carries per-kernel traffic
+@pytest.mark.parametrize("workload", sorted(bench.TRAFFIC_FILES))
+def test_committed_summaries_parse(workload):
+    # each summary the bench reads names the command that made it, on the
+    # same workload, and carries traffic for the kernel its file is named for
+    name = bench.TRAFFIC_FILES[workload]
     text = open(os.path.join(ROOT, name)).read()
-    assert "rocprofv3 --kernel-trace --stats" in text and "python3 bench.py" in text
+    assert "rocprofv3 --kernel-trace --stats" in text and f"python3 bench.py --workload {workload} " in text
     data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-    cast = data["kernels"]["group_cast_kernel"]
-    assert cast["fetch_bytes"] > 0 and cast["write_bytes"] > 0
+    kernel = os.path.basename(name).split("-", 1)[0]
+    k = data["kernels"][kernel]
+    assert k["fetch_bytes"] > 0 and k["write_bytes"] > 0
     assert np.isclose(data["fetch_scale"], 2.0, rtol=0.01) and np.isclose(data["write_scale"], 1.0, rtol=0.01)
+
+
+def test_committed_summaries_match_the_current_code():
+    # every kernel entry of every committed summary was taken on the code as
+    # it is now (else the bench would report its traffic as unknown)
+    import glob
+    stale = []
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        text = open(path).read()
+        data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        for kernel, entry in data["kernels"].items():
+            if entry.get("source_sha256") != profiling.source_sha256(kernel):
+                stale.append((os.path.basename(path), kernel))
+    assert not stale, stale
 
 
 def test_four_over_six_row_accounting():
