@@ -57,6 +57,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+EVENT_STRIDE = 10  # timed steps per step with per-launch events
 METRIC = "grouped NVFP4 amax+cast HBM GB/s (bytes in+out) and % of MI355X peak BW"
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, per workload
 TRAFFIC_FILES = {"deepseek_share": "profiles/group_cast_kernel-deepseek_share_e32_k7168_m65536.md",
@@ -208,7 +209,8 @@ SIDE_CPU_REPS = {"tiny": 5, "outliers": 5, "down_proj": 1}
 def measure_step(B, torch, tev, w, x, out, steps: int, warmup: int, settle_ms: float) -> dict:
     """Time `steps` back-to-back steps of the whole path on workload `w` (x and
     the outputs already on the device): wall clock between two device
-    synchronisations, plus per-launch times from HIP events on the stream."""
+    synchronisations, plus per-launch times from HIP events on the stream
+    around the launches of every EVENT_STRIDE-th of those steps."""
     splits = [int(v) for v in w.splits]
     k = w.k
     fused = w.rowwise and not w.columnwise
@@ -240,15 +242,19 @@ def measure_step(B, torch, tev, w, x, out, steps: int, warmup: int, settle_ms: f
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[tev.new() for _ in range(3)] for _ in range(steps)]
+    # HIP events around the launches of every EVENT_STRIDE-th timed step give
+    # the per-kernel times: an event record costs a few microseconds of
+    # stream time, which around every step would add ~2% to the expert-share
+    # step and half again to the small ones
+    events = {i: [tev.new() for _ in range(3)] for i in range(0, steps, EVENT_STRIDE)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i])
+        step(events.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    first_ms = float(np.mean([tev.elapsed_ms(e[0], e[1]) for e in events]))
-    second_ms = float(np.mean([tev.elapsed_ms(e[1], e[2]) for e in events]))
+    first_ms = float(np.mean([tev.elapsed_ms(e[0], e[1]) for e in events.values()]))
+    second_ms = float(np.mean([tev.elapsed_ms(e[1], e[2]) for e in events.values()]))
     nbytes = algorithmic_bytes(w.sum_m, k, w.num_experts, w.rowwise, w.columnwise)
     ms_per_step = wall * 1e3 / steps
     if fused or small:
