@@ -336,6 +336,8 @@ def main():
                     help="also run a plain 1 GiB device-to-device copy (3 times, untimed) so that a "
                          "rocprofv3 --pmc run can scale FETCH_SIZE / WRITE_SIZE by a copy of known size")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
