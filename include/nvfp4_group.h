@@ -50,6 +50,8 @@
  * call that fails a check enqueues nothing and returns a negative status;
  * launch failures return NVFP4G_EHIP.  A direction is produced when its data
  * pointer is non-NULL (its scale pointer and amax must then be non-NULL).
+ * The library keeps no state between calls: calls from several host threads,
+ * on different streams and buffers, are independent of each other.
  */
 #ifndef NVFP4_GROUP_H_
 #define NVFP4_GROUP_H_
