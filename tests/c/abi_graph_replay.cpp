@@ -6,7 +6,8 @@
 // status word is cleared and every output is filled with a sentinel byte
 // (all outside the graph); after it the outputs and the status are copied
 // back.  The library's host-side checks are exercised first: a call with
-// K = 15 must be refused with NVFP4G_EINVAL before anything is launched.
+// K = 15 must be refused with NVFP4G_EINVAL before anything is launched; and
+// the captured graph must hold kernel nodes only (no memset nodes).
 //
 //   usage: abi_graph_replay <in.bin> <out.bin>
 //   in.bin  (little-endian): int64 m_cap, k, E, R; int32 offs[R][E]
@@ -106,9 +107,23 @@ int main(int argc, char** argv) {
     return 1;
   }
   HIP_OK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+  // every node must be a kernel: the amax zero-fill is a kernel, never a
+  // memset node
   size_t nodes = 0;
   HIP_OK(hipGraphGetNodes(graph, nullptr, &nodes));
-  std::printf("captured %zu graph nodes\n", nodes);
+  std::vector<hipGraphNode_t> list(nodes);
+  HIP_OK(hipGraphGetNodes(graph, list.data(), &nodes));
+  size_t kernels = 0;
+  for (size_t i = 0; i < nodes; ++i) {
+    hipGraphNodeType type;
+    HIP_OK(hipGraphNodeGetType(list[i], &type));
+    kernels += type == hipGraphNodeTypeKernel;
+  }
+  std::printf("captured %zu graph nodes, %zu kernels\n", nodes, kernels);
+  if (nodes == 0 || kernels != nodes) {
+    std::fprintf(stderr, "the capture holds nodes other than kernels\n");
+    return 1;
+  }
 
   std::FILE* out = std::fopen(argv[2], "wb");
   if (!out) {

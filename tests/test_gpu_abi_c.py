@@ -5,8 +5,8 @@ page, Description: the graph-safe calls read the routing from device
 offsets, so one capture replays under changed routing).  Every replay's
 amax, FP4 bytes and E4M3 scales must equal the oracle's for that routing,
 rows and columnwise bytes beyond the routed total must keep the sentinel
-byte, the device status must be 0, and the library must refuse K = 15 on the
-host before launching anything."""
+byte, the device status must be 0, the library must refuse K = 15 on the
+host before launching anything, and the capture must hold kernel nodes only."""
 import os
 import subprocess
 
@@ -44,6 +44,8 @@ def _run(tmp_path, m_cap, k, routings, seed):
     r = subprocess.run([EXE, str(inp), str(outp)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "refused K = 15" in r.stdout
+    # the capture holds kernels only (the program fails otherwise)
+    assert any(line.startswith("captured ") and line.endswith(" kernels") for line in r.stdout.splitlines())
     return x, r.stdout, np.fromfile(outp, dtype=np.uint8)
 
 
