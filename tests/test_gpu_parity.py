@@ -382,6 +382,11 @@ SMALL_ONE_LAUNCH = [
     ([128, 0, 128], 272, "rowscale", 94),           # ragged 512-column chunk
     ([1280, 512], 48, "student", 95),               # gradient-like values, long experts
     ([128, 128, 128], 16, "sparse", 96),            # all-zero blocks and rows
+    # expert counts that are not multiples of 8 (an expert's work-groups
+    # share an XCD; indexes past the last expert exit)
+    ([128] * 9, 64, "normal", 99),
+    ([128, 0] * 16 + [256], 32, "rowscale", 100),
+    ([0] * 70 + [128] * 3, 128, "student", 101),
 ]
 
 
@@ -394,6 +399,22 @@ def test_small_input_one_launch(splits, k, dist, seed):
 def test_small_input_one_launch_columnwise_only():
     check_small(synth.random_case(97, [256, 0, 128], 96, "rowscale"), rowwise=False, columnwise=True,
                 entry="quantize")
+
+
+def test_small_input_graphsafe_one_launch_many_experts():
+    # device routing with 1000 experts over a 128-row capacity: every row in
+    # expert 777, all others empty (column amax 0); one launch
+    rng = np.random.default_rng(102)
+    cap, k, E = 128, 512, 1000
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((cap, k)).astype(np.float32))
+    splits = [0] * E
+    splits[777] = 128
+    assert cap * k <= B.SMALL_MAX_EXPERT_ELEMS
+    log("graph-safe one launch, 1000 experts")
+    gs, status = _graphsafe(to_device(xb), E, B.offsets_from_splits(splits), cap, prefill=0x5A, entry="quantize")
+    assert status == 0
+    assert_guards(gs)
+    assert_equal_outputs(to_numpy(gs), oracle_ref(synth.Workload("many", xb, np.array(splits, np.int64))))
 
 
 def test_small_input_graphsafe_one_launch():
