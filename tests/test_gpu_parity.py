@@ -402,15 +402,17 @@ def test_small_input_one_launch_columnwise_only():
 
 
 def test_small_input_graphsafe_one_launch_many_experts():
-    # device routing with 1000 experts over a 128-row capacity: every row in
-    # expert 777, all others empty (column amax 0); one launch
+    # device routing with 4093 experts (near the limit, not a multiple of the
+    # 8 XCDs) over a 128-row capacity: every row in expert 4000, all others
+    # empty (column amax 0); one launch
     rng = np.random.default_rng(102)
-    cap, k, E = 128, 512, 1000
+    cap, k, E = 128, 512, 4093
+    assert E <= B.MAX_EXPERTS_DEVICE
     xb = synth.f32_to_bf16_bits(rng.standard_normal((cap, k)).astype(np.float32))
     splits = [0] * E
-    splits[777] = 128
+    splits[4000] = 128
     assert cap * k <= B.SMALL_MAX_EXPERT_ELEMS
-    log("graph-safe one launch, 1000 experts")
+    log("graph-safe one launch, 4093 experts")
     gs, status = _graphsafe(to_device(xb), E, B.offsets_from_splits(splits), cap, prefill=0x5A, entry="quantize")
     assert status == 0
     assert_guards(gs)
